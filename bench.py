@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Paged attention throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch of synthetic input that is
+already resident in HBM: for the decode workloads one ``paged_attn_decode``
+call per layer (block-table walk, K/V gather, QK, online softmax, PV,
+partition merge), for the multi-token workloads one ``paged_attn_multiq`` call.
+Several replicas of the K/V pool are rotated between steps so that the 256 MB
+Infinity Cache cannot serve a step from the previous one's reads.
+
+Prints ONE JSON line: throughput on algorithmic KV bytes (every visible token's
+K and V read once: sum_s L_s * 2 * Hk * D * elem), tokens/s, the roofline of
+the dominant launch (timed live with HIP events on the launch stream) and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (KV bytes) + % of peak; tokens/s"
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+DECODE = ("llama3_8b_decode", "llama3_70b_decode", "shared_prefix_mix", "tiny_fp32")
+MULTIQ = ("spec_verify", "chunked_prefill")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="llama3_8b_decode", choices=DECODE + MULTIQ)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="K/V pool replicas rotated between steps (default: >= 2 GiB in total)")
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library's)")
+    ap.add_argument("--layers", type=int, default=None, help="override layer count (70B workload)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling HBM counters) and exit")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# workload set-up
+# ---------------------------------------------------------------------------
+
+def make_structure(name, seed, layers):
+    from paged_kv_cache_289_amd import workloads as W
+    if name == "llama3_70b_decode":
+        return W.llama3_70b_decode(seed, layers=layers or 80)
+    return W.NAMED[name](seed)
+
+
+def kv_bytes_of(st) -> int:
+    """Algorithmic KV bytes of one call: every visible token's K and V, once."""
+    return int(st.context_lens.astype(np.int64).sum()) * 2 * st.num_kv_heads * st.head_dim * \
+        st.elem_bytes
+
+
+def unique_kv_bytes_of(st) -> int:
+    """Bytes of distinct (block, slot) pairs the call touches (shared prefixes count once)."""
+    seen = set()
+    B = st.block_size
+    for s in range(st.num_seqs):
+        L = int(st.context_lens[s])
+        for j in range(-(-L // B)):
+            seen.add((int(st.block_tables[s, j]), min(B, L - j * B)))
+    tokens = 0
+    per_block = {}
+    for b, n in seen:
+        per_block[b] = max(per_block.get(b, 0), n)
+    tokens = sum(per_block.values())
+    return tokens * 2 * st.num_kv_heads * st.head_dim * st.elem_bytes
+
+
+def flops_of(st, causal=True) -> int:
+    """QK and PV multiply-adds (2 flops each) over every visible (row, head, key)."""
+    tot = 0
+    for s in range(st.num_seqs):
+        n, L = int(st.q_lens[s]), int(st.context_lens[s])
+        vis = sum((L - n + i + 1) if causal else L for i in range(n))
+        tot += vis
+    return 4 * st.head_dim * st.num_heads * tot
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_289_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, src_hash: str):
+    """HBM bytes per launch of the main kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for a
+    1 GiB copy), or None when there is none for the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(st, dv, budget_s, is_multiq):
+    import torch
+    import oracle.paged_attention as OP
+    from paged_kv_cache_289_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_limits, threadpool_info
+    except ImportError:                      # pragma: no cover
+        threadpool_limits = None
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    vals = {k: W.torch_to_host(v, st.dtype) for k, v in dv.items()}
+    per_tok = 2 * st.num_kv_heads * st.head_dim * st.elem_bytes
+    order = list(np.argsort(-st.context_lens))[::max(1, st.num_seqs // 16)] or [0]
+    done, spent, seqs_used = 0, 0.0, []
+    for s in list(order) + [s for s in range(st.num_seqs) if s not in order]:
+        if spent >= budget_s:
+            break
+        t0 = time.perf_counter()
+        if is_multiq:
+            OP.paged_multiq(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
+                            st.context_lens, st.q_offsets, st.block_size, st.scale, st.dtype,
+                            seqs=[int(s)])
+        else:
+            OP.paged_decode(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
+                            st.context_lens, st.block_size, st.scale, st.dtype, seqs=[int(s)])
+        spent += time.perf_counter() - t0
+        done += int(st.context_lens[s]) * per_tok
+        seqs_used.append(int(s))
+    if ctx is not None:
+        ctx.unregister() if hasattr(ctx, "unregister") else None
+    gbps = done / spent / 1e9 if spent > 0 else None
+    return {"value": round(gbps, 4) if gbps else None, "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(seqs_used)} of {st.num_seqs} sequences of one layer "
+                      f"({done / 2**20:.1f} MiB of KV) in {spent:.1f} s, fp64 NumPy, "
+                      f"BLAS threads <= {cores}"}
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the attention "
+              f"path shards by KV head or by sequence with no exchange, so one GPU's share "
+              f"is the kernel at its real shape).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from paged_kv_cache_289_amd import ops, workloads as W
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if a.copy_calibration:
+        n = 1 << 30
+        x = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}))
+        return
+
+    is_multiq = a.workload in MULTIQ
+    st = make_structure(a.workload, a.seed, a.layers)
+    layers = st.layers
+    kv_call = kv_bytes_of(st)
+    steps = a.steps if a.steps is not None else (10 if layers > 1 else 100)
+    warm = a.warmup if a.warmup is not None else (2 if layers > 1 else 10)
+    log(f"[bench] {st.name}: {json.dumps(st.summary())}")
+
+    # inputs resident in HBM: q, tables, lens; K/V pool replicas (one per layer for the
+    # 80-layer workload, which already spans 80 GiB)
+    tables = torch.from_numpy(st.block_tables).to(dev)
+    lens = torch.from_numpy(st.context_lens).to(dev)
+    qoff = torch.from_numpy(st.q_offsets).to(dev)
+    dv = W.device_values(st, dev)
+    pool_bytes = 2 * dv["k_cache"].numel() * dv["k_cache"].element_size()
+    if layers > 1:
+        pools = [(dv["k_cache"], dv["v_cache"])]
+        for l in range(1, layers):
+            d = W.device_values(st, dev, layer=l)
+            pools.append((d["k_cache"], d["v_cache"]))
+            del d
+            if l % 10 == 0:
+                log(f"[bench] generated {l + 1}/{layers} layers")
+        reps = 1
+    else:
+        reps = a.replicas or max(1, math.ceil(2 * 2**30 / max(pool_bytes, 1)))
+        reps = min(reps, 16)
+        pools = [(dv["k_cache"], dv["v_cache"])] + [
+            (dv["k_cache"].clone(), dv["v_cache"].clone()) for _ in range(reps - 1)]
+    q = dv["q"]
+    out = torch.empty(q.shape, dtype=q.dtype, device=dev)
+    H, D = st.num_heads, st.head_dim
+    part = a.partition or ops.default_partition(st.num_seqs, st.num_kv_heads, st.block_size,
+                                                st.max_context_len, st.max_q_len)
+    wsb = ops.workspace_size(st.num_seqs, st.total_q, st.max_q_len, H, st.num_kv_heads, D,
+                             st.block_size, st.max_context_len, part)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    if is_multiq:
+        prepared = ops.prepare_multiq(q, pools[0][0], pools[0][1], tables, lens, qoff, st.scale,
+                                      st.max_context_len, st.max_q_len, out,
+                                      partition_tokens=part, workspace=ws, stream=stream)
+    else:
+        prepared = ops.prepare_decode(q, pools[0][0], pools[0][1], tables, lens, st.scale,
+                                      st.max_context_len, out, partition_tokens=part,
+                                      workspace=ws, stream=stream)
+    call = prepared.run
+
+    calls_per_step = layers
+    npools = len(pools)
+    for i in range(warm * calls_per_step):
+        call(*pools[i % npools])
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps * calls_per_step)]
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps * calls_per_step)]
+    for e0, e1 in kev:            # materialize the events before the timed region
+        e0.record(stream)
+        e1.record(stream)
+    kev_ptrs = [(ctypes.c_void_p(e0.cuda_event), ctypes.c_void_p(e1.cuda_event)) for e0, e1 in kev]
+    set_events = ops.LIB.paged_attn_set_kernel_events
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    k = 0
+    for step in range(steps):
+        for c in range(calls_per_step):
+            kc, vc = pools[(step * calls_per_step + c) % npools] if layers == 1 else pools[c]
+            set_events(*kev_ptrs[k])
+            ev[k][0].record(stream)
+            call(kc, vc)
+            ev[k][1].record(stream)
+            k += 1
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ops.set_kernel_events(None, None)
+    kernel_ms = np.array([s.elapsed_time(e) for s, e in kev])
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per_call_ms = np.array([s.elapsed_time(e) for s, e in ev])
+    ms_per_step = total_ms / steps
+    call_ms = float(per_call_ms.mean())
+
+    kv_step = kv_call * calls_per_step
+    value = kv_step / (ms_per_step * 1e-3) / 1e9
+    tokens_step = st.total_q
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": st.dtype, "data": "synthetic",
+        "config": {
+            "workload": st.name, "num_seqs": st.num_seqs, "num_heads": H,
+            "num_kv_heads": st.num_kv_heads, "head_dim": D, "block_size": st.block_size,
+            "sum_context": int(st.context_lens.sum()), "max_context": st.max_context_len,
+            "query_tokens": st.total_q, "layers": layers, "partition_tokens": part,
+            "pool_replicas": reps if layers == 1 else layers, "seed": a.seed,
+            "pool_blocks": st.num_blocks,
+        },
+        "frac_of_peak_hbm": round(value / PEAK_HBM_GBPS, 4),
+        "tokens_per_s": round(tokens_step / (ms_per_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_step,
+        "call_ms": {"mean": round(call_ms, 5), "p10": round(float(np.percentile(per_call_ms, 10)), 5),
+                    "p50": round(float(np.median(per_call_ms)), 5),
+                    "p90": round(float(np.percentile(per_call_ms, 90)), 5)},
+        "wall_s_timed": round(wall, 3),
+        "source_hash": source_hash(),
+    }
+    if a.workload == "shared_prefix_mix":
+        ub = unique_kv_bytes_of(st)
+        res["unique_kv_bytes_per_step"] = ub
+        res["unique_GBps"] = round(ub / (ms_per_step * 1e-3) / 1e9, 2)
+
+    # roofline of the dominant kernel (the call's main kernel, bracketed by HIP events that
+    # the library records on the launch stream)
+    kern_ms = float(kernel_ms.mean())
+    res["kernel_ms"] = {"mean": round(kern_ms, 5), "p50": round(float(np.median(kernel_ms)), 5)}
+    if is_multiq and a.workload == "chunked_prefill":
+        fl = flops_of(st)
+        ach = fl / (kern_ms * 1e-3) / 1e12
+        basis = None
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    else:
+        basis = res.get("unique_kv_bytes_per_step", kv_step) // calls_per_step
+        ach = basis / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBPS, 4)}
+    roof["traffic"] = measured_traffic(st.name, res["source_hash"])
+    roof["kernel"] = "multi-query main kernel" if is_multiq else "decode partial kernel"
+    roof["algorithmic_bytes_per_launch"] = int(basis) if basis is not None else None
+    if is_multiq:
+        res["tflops"] = round(flops_of(st) / (call_ms * 1e-3) / 1e12, 2)
+    res["roofline"] = roof
+
+    if a.cpu_seconds > 0:
+        log("[bench] timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline(st, {"q": dv["q"], "k_cache": pools[0][0],
+                                                "v_cache": pools[0][1]},
+                                           a.cpu_seconds, is_multiq)
+    else:
+        res["cpu_baseline"] = None
+
+    line = json.dumps(res)
+    print(line, flush=True)
+    if a.json_out:
+        with open(a.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

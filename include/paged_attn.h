@@ -1,0 +1,178 @@
+/*
+ * paged_attn.h -- C ABI of libpagedattn.so, paged attention for MI355X (gfx950).
+ *
+ * What the library computes.  The KV cache of every sequence is cut into
+ * fixed-size blocks (16 tokens by default) that sit anywhere in one shared
+ * physical pool; a per-sequence block table maps logical positions to physical
+ * blocks, and the attention kernel gathers K/V from the scattered blocks
+ * through it ("Local_LLM_03_vLLM_Architecture", PagedAttention slide; "vLLM:
+ * LLM Inference That Doesn't Waste Your GPU", section "PagedAttention: virtual
+ * memory for KV").  Each query token attends over every prior cached token
+ * ("Local_LLM_03_vLLM_Architecture", KV-cache slide).  Several sequences may
+ * point at the same physical blocks for a shared prompt prefix ("Scaling
+ * inference with vLLM", prefix-sharing paragraph); K/V are only read, so that
+ * aliasing is always allowed.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, keeps no pointer after return, and never synchronizes:
+ *    work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *  - Element counts are in elements, byte counts in bytes.
+ *  - Pool layout: k_cache and v_cache are separate, contiguous
+ *        [num_blocks][num_kv_heads][block_size][head_dim]
+ *    arrays.  Token t of sequence s lives in physical block
+ *    block_tables[s * max_blocks_per_seq + t / block_size], slot t % block_size.
+ *    block_tables is int32 [num_seqs][max_blocks_per_seq], row-major; only the
+ *    first ceil(context_lens[s] / block_size) entries of row s are read.
+ *  - context_lens[s] (int32, device) counts every key the queries of s may
+ *    see, including the query tokens' own K/V, which the caller has already
+ *    written into the pool.  Values <= 0 give zero output rows.
+ *  - Grouped-query attention: query head h reads KV head h / (num_heads /
+ *    num_kv_heads) (contiguous groups).
+ *  - Scores are scale * <q, k>; softmax accumulates in fp32.
+ *  - Scalar arguments are validated on the host before any HIP call; a bad
+ *    argument returns a negative pa_status and enqueues nothing.  Device
+ *    contents are trusted: context_lens[s] must not exceed max_context_len and
+ *    every table entry that is read must be in [0, num_blocks).
+ *    paged_attn_check_inputs() verifies both on the device when in doubt.
+ *  - Supported: dtype in {PA_F32, PA_F16, PA_BF16} (q, k_cache, v_cache share
+ *    it); out_dtype PA_F32 or equal to dtype; head_dim in {64, 128};
+ *    block_size in {8, 16, 32}; num_heads % num_kv_heads == 0 with
+ *    num_heads / num_kv_heads <= 16.  Anything else: PA_ERR_UNSUPPORTED.
+ *  - Thread safety: reentrant; the only global state is a per-device cache of
+ *    device properties.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  PA_ERR_SHAPE = -2,       /* inconsistent or negative sizes                   */
+  PA_ERR_UNSUPPORTED = -3, /* dtype / head_dim / block_size / group not built  */
+  PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required       */
+  PA_ERR_HIP = -5          /* a HIP launch or runtime call failed              */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Opaque to this header; it is a hipStream_t. */
+typedef void* pa_stream_t;
+
+/*
+ * Bytes of device workspace that paged_attn_decode (total_q == num_seqs,
+ * max_q_len == 1) or paged_attn_multiq needs for these shapes when called
+ * with the same partition_tokens (0 = the library's choice).  The workspace
+ * holds fp32 (max, sum, unnormalized output) partials of each context
+ * partition for the log-sum-exp merge.  0 is a legal answer (no merge
+ * needed).  Returns 0 as well for arguments the entry points would reject.
+ */
+size_t paged_attn_workspace_size(int num_seqs, int total_q, int max_q_len, int num_heads,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int max_context_len, int partition_tokens);
+
+/*
+ * Decode step: one query token per sequence.
+ *   out  [num_seqs][num_heads][head_dim]  (out_dtype)
+ *   q    [num_seqs][num_heads][head_dim]  (dtype)
+ * For each (s, h): out = sum_t softmax_t(scale * <q, k_t>) v_t over the
+ * context_lens[s] keys of KV head h / G of sequence s, gathered through the
+ * block table (the decode step's attention over every prior token,
+ * "Local_LLM_03_vLLM_Architecture", KV-cache and PagedAttention slides).
+ * Long contexts are split into partitions of partition_tokens tokens
+ * (0 = library's choice; otherwise a positive multiple of block_size) whose
+ * partial results are merged by log-sum-exp in a second kernel.
+ * workspace may be NULL when paged_attn_workspace_size() returns 0.
+ */
+int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int max_blocks_per_seq,
+                      int max_context_len, float scale, int dtype, int out_dtype,
+                      int partition_tokens, void* workspace, size_t workspace_bytes,
+                      pa_stream_t stream);
+
+/*
+ * Several query tokens per sequence: the k guessed tokens that speculative
+ * decoding verifies in one pass ("Scaling inference with vLLM", speculative
+ * decoding paragraph) or a chunk of a prompt processed as one prefill batch
+ * ("Local_LLM_03_vLLM_Architecture", chunked-prefill slide).
+ *   out  [total_q][num_heads][head_dim]  (out_dtype)
+ *   q    [total_q][num_heads][head_dim]  (dtype)
+ *   q_offsets  int32 [num_seqs + 1], device: rows of sequence s are
+ *              q_offsets[s] .. q_offsets[s+1]-1, q_offsets[0] == 0,
+ *              q_offsets[num_seqs] == total_q, n_s = q_offsets[s+1]-q_offsets[s]
+ *              <= max_q_len.
+ * The n_s rows are the last n_s positions of the context.  With causal != 0,
+ * row i of s sees keys t <= context_lens[s] - n_s + i (requires
+ * context_lens[s] >= n_s); with causal == 0 every row sees all keys.
+ * The contraction runs on bf16/fp16 MFMA with fp32 accumulation (dtype PA_F32
+ * runs a vector-ALU path).  Other conventions as paged_attn_decode.
+ */
+int paged_attn_multiq(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* q_offsets, int num_seqs, int total_q, int max_q_len,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
+                      int causal, int dtype, int out_dtype, int partition_tokens,
+                      void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * Block-table walk alone: copy each sequence's K and V, in logical order, out
+ * of the paged pool into contiguous arrays (the gather that the attention
+ * kernels fuse; "Local_LLM_03_vLLM_Architecture", PagedAttention slide).
+ *   k_out, v_out   [token_offsets[num_seqs]][num_kv_heads][head_dim] (dtype)
+ *   token_offsets  int32 [num_seqs + 1], device; token t of sequence s goes
+ *                  to row token_offsets[s] + t; token_offsets[s+1] -
+ *                  token_offsets[s] must equal context_lens[s].
+ * Bytes are copied unchanged (bit-exact).
+ */
+int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* token_offsets, int num_seqs, int num_kv_heads, int head_dim,
+                    int block_size, int num_blocks, int max_blocks_per_seq, int dtype,
+                    pa_stream_t stream);
+
+/*
+ * Device-side check of the contents the attention entry points trust:
+ * counts sequences whose context_lens[s] is negative or above
+ * max_context_len, and table entries among the first
+ * ceil(context_lens[s] / block_size) of each row that fall outside
+ * [0, num_blocks).  Writes the count (int32) to *bad_count (device); it is
+ * zero when the inputs are safe to pass to the attention entry points.
+ */
+int paged_attn_check_inputs(const int32_t* block_tables, const int32_t* context_lens,
+                            int num_seqs, int block_size, int num_blocks, int max_blocks_per_seq,
+                            int max_context_len, int32_t* bad_count, pa_stream_t stream);
+
+/*
+ * Profiling aid.  With both arguments non-NULL (hipEvent_t handles), every
+ * later paged_attn_decode / paged_attn_multiq call made from this host thread
+ * records `start` on its stream right before its main kernel and `stop` right
+ * after it (a partition merge, if any, runs after `stop`), so the elapsed time
+ * between them is that kernel's duration.  NULL, NULL turns it off.  The
+ * events are caller-owned and must outlive the calls that record them.
+ * Returns PA_ERR_NULL if exactly one argument is NULL.
+ */
+int paged_attn_set_kernel_events(void* start, void* stop);
+
+/* Partition length (tokens) that the library picks when partition_tokens is 0. */
+int paged_attn_default_partition(int num_seqs, int num_kv_heads, int block_size,
+                                 int max_context_len, int max_q_len);
+
+/* Static description of a status code. */
+const char* paged_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,252 @@
+// C-ABI host layer of libpagedattn.so: argument validation (pure host code,
+// before any HIP call), the partition planner, workspace sizing and dispatch to
+// the kernel launchers.  Declarations and conventions: include/paged_attn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "pa_internal.h"
+
+namespace pa {
+hipError_t launch_merge_rows(int head_dim, int num_seqs, const AttnArgs& a, hipStream_t st);
+}
+
+namespace {
+
+bool dtype_ok(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
+int elem_bytes(int dt) { return dt == PA_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// events of paged_attn_set_kernel_events, per host thread
+thread_local pa::KernelEvents t_events;
+
+// Shared shape checks of the attention entry points.  Returns PA_OK or an error.
+int check_attn_shapes(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, int max_context_len, int dtype,
+                      int out_dtype, int partition_tokens, float scale) {
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 ||
+      num_blocks < 1 || max_blocks_per_seq < 1 || max_context_len < 0 || partition_tokens < 0)
+    return PA_ERR_SHAPE;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (!dtype_ok(dtype) || !(out_dtype == PA_F32 || out_dtype == dtype)) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 8 && block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (num_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+  if (partition_tokens > 0 && partition_tokens % block_size != 0) return PA_ERR_SHAPE;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+int resolve_partition(int partition_tokens, int num_seqs, int num_kv_heads, int block_size,
+                      int max_context_len, int max_q_len) {
+  return partition_tokens > 0
+             ? partition_tokens
+             : paged_attn_default_partition(num_seqs, num_kv_heads, block_size, max_context_len,
+                                            max_q_len);
+}
+
+// Workspace layout: fp32 (max, sum) pairs [rows][H][P], then fp32 partial
+// outputs [rows][H][P][D].
+size_t workspace_bytes_for(int rows, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                           int max_parts) {
+  if (max_parts <= 1) return 0;
+  (void)num_seqs;
+  (void)num_kv_heads;
+  return (size_t)rows * num_heads * max_parts * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+void split_workspace(void* ws, int rows, int num_heads, int max_parts, int head_dim,
+                     pa::AttnArgs* a) {
+  float* base = static_cast<float*>(ws);
+  a->ws_ml = base;
+  a->ws_o = base + (size_t)rows * num_heads * max_parts * 2;
+  (void)head_dim;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_set_kernel_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return PA_ERR_NULL;
+  t_events.start = static_cast<hipEvent_t>(start);
+  t_events.stop = static_cast<hipEvent_t>(stop);
+  return PA_OK;
+}
+
+const char* paged_attn_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "inconsistent or negative sizes";
+    case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, block_size, group or alignment";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int paged_attn_default_partition(int num_seqs, int num_kv_heads, int block_size,
+                                 int max_context_len, int max_q_len) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)max_context_len;
+  int part = max_q_len > 1 ? 512 : 2048;
+  if (part % block_size) part = ceil_div(part, block_size) * block_size;
+  return part;
+}
+
+size_t paged_attn_workspace_size(int num_seqs, int total_q, int max_q_len, int num_heads,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int max_context_len, int partition_tokens) {
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_heads < 1 || num_kv_heads < 1 ||
+      head_dim < 1 || block_size < 1 || max_context_len < 0 || partition_tokens < 0)
+    return 0;
+  if (partition_tokens > 0 && partition_tokens % block_size) return 0;
+  const int part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, block_size,
+                                     max_context_len, max_q_len);
+  const int max_parts = ceil_div(max_context_len, part);
+  return workspace_bytes_for(total_q, num_seqs, num_heads, num_kv_heads, head_dim, max_parts);
+}
+
+int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
+                      int dtype, int out_dtype, int partition_tokens, void* workspace,
+                      size_t workspace_bytes, pa_stream_t stream) {
+  int rc = check_attn_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             max_blocks_per_seq, max_context_len, dtype, out_dtype,
+                             partition_tokens, scale);
+  if (rc != PA_OK) return rc;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
+
+  const int part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, block_size,
+                                     max_context_len, 1);
+  const int max_parts = std::max(1, ceil_div(max_context_len, part));
+  const size_t need =
+      workspace_bytes_for(num_seqs, num_seqs, num_heads, num_kv_heads, head_dim, max_parts);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PA_ERR_WORKSPACE;
+
+  pa::AttnArgs a{};
+  a.out = out;
+  if (need > 0) split_workspace(workspace, num_seqs, num_heads, max_parts, head_dim, &a);
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.q_offsets = nullptr;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.part = part;
+  a.max_parts = max_parts;
+  a.max_q_len = 1;
+  a.causal = 0;
+  a.out_dtype = out_dtype;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pa::launch_decode(dtype, head_dim, block_size, a.group, num_seqs, a,
+                                   static_cast<hipStream_t>(stream), t_events);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int paged_attn_multiq(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* q_offsets, int num_seqs, int total_q, int max_q_len,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
+                      int causal, int dtype, int out_dtype, int partition_tokens,
+                      void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  int rc = check_attn_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             max_blocks_per_seq, max_context_len, dtype, out_dtype,
+                             partition_tokens, scale);
+  if (rc != PA_OK) return rc;
+  if (total_q < 0 || max_q_len < 0 || (total_q > 0 && max_q_len < 1)) return PA_ERR_SHAPE;
+  if ((int64_t)max_q_len * num_seqs < total_q) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || total_q == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !q_offsets)
+    return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
+
+  const int part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, block_size,
+                                     max_context_len, max_q_len);
+  const int max_parts = std::max(1, ceil_div(max_context_len, part));
+  const int rows = total_q;
+  const size_t need =
+      workspace_bytes_for(rows, num_seqs, num_heads, num_kv_heads, head_dim, max_parts);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PA_ERR_WORKSPACE;
+
+  pa::AttnArgs a{};
+  a.out = out;
+  if (need > 0) split_workspace(workspace, rows, num_heads, max_parts, head_dim, &a);
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.q_offsets = q_offsets;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.part = part;
+  a.max_parts = max_parts;
+  a.max_q_len = max_q_len;
+  a.causal = causal ? 1 : 0;
+  a.out_dtype = out_dtype;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pa::launch_multiq(dtype, head_dim, block_size, a.group, num_seqs, a,
+                                   static_cast<hipStream_t>(stream), t_events);
+  if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* token_offsets, int num_seqs, int num_kv_heads, int head_dim,
+                    int block_size, int num_blocks, int max_blocks_per_seq, int dtype,
+                    pa_stream_t stream) {
+  if (num_seqs < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1 ||
+      max_blocks_per_seq < 1)
+    return PA_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if ((head_dim * elem_bytes(dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!k_out || !v_out || !k_cache || !v_cache || !block_tables || !context_lens ||
+      !token_offsets)
+    return PA_ERR_NULL;
+  if (!aligned16(k_out) || !aligned16(v_out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  hipError_t e = pa::launch_gather(k_out, v_out, k_cache, v_cache, block_tables, context_lens,
+                                    token_offsets, num_seqs, num_kv_heads, head_dim, block_size,
+                                    max_blocks_per_seq, max_blocks_per_seq, elem_bytes(dtype),
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int paged_attn_check_inputs(const int32_t* block_tables, const int32_t* context_lens,
+                            int num_seqs, int block_size, int num_blocks, int max_blocks_per_seq,
+                            int max_context_len, int32_t* bad_count, pa_stream_t stream) {
+  if (num_seqs < 0 || block_size < 1 || num_blocks < 1 || max_blocks_per_seq < 1 ||
+      max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (!bad_count || (num_seqs > 0 && (!block_tables || !context_lens))) return PA_ERR_NULL;
+  hipError_t e = pa::launch_check(block_tables, context_lens, num_seqs, block_size, num_blocks,
+                                  max_blocks_per_seq, max_context_len, bad_count,
+                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

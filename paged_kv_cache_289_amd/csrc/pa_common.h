@@ -1,0 +1,159 @@
+// Device helpers shared by the gfx950 paged-attention kernels: element traits
+// for the three storage types, 16-byte vector loads, bf16/f16 dot2 and
+// conversions, and wave64 cross-lane reductions built on DPP.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// element traits: one 16-byte vector = kPerVec elements
+// ---------------------------------------------------------------------------
+template <int DT> struct Elem;
+
+template <> struct Elem<PA_F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerVec = 4;
+  // partial dot product of the 4 elements held in one vector
+  __device__ static inline float dot(const uint4& q, const uint4& k, float acc) {
+    acc = __builtin_fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+    acc = __builtin_fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+    acc = __builtin_fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+    acc = __builtin_fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+    return acc;
+  }
+  __device__ static inline void to_float(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+};
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <> struct Elem<PA_BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerVec = 8;
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+  }
+  __device__ static inline float dot(const uint4& q, const uint4& k, float acc) {
+    acc = dot2(q.x, k.x, acc);
+    acc = dot2(q.y, k.y, acc);
+    acc = dot2(q.z, k.z, acc);
+    acc = dot2(q.w, k.w, acc);
+    return acc;
+  }
+  __device__ static inline void to_float(const uint4& v, float* f) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+  }
+};
+
+template <> struct Elem<PA_F16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerVec = 8;
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  acc, false);
+  }
+  __device__ static inline float dot(const uint4& q, const uint4& k, float acc) {
+    acc = dot2(q.x, k.x, acc);
+    acc = dot2(q.y, k.y, acc);
+    acc = dot2(q.z, k.z, acc);
+    acc = dot2(q.w, k.w, acc);
+    return acc;
+  }
+  __device__ static inline void pair(uint32_t w, float* f) {
+    f16x2_t h = __builtin_bit_cast(f16x2_t, w);
+    f[0] = (float)h.x;
+    f[1] = (float)h.y;
+  }
+  __device__ static inline void to_float(const uint4& v, float* f) {
+    pair(v.x, f); pair(v.y, f + 2); pair(v.z, f + 4); pair(v.w, f + 6);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// output conversion (round to nearest even)
+// ---------------------------------------------------------------------------
+__device__ inline uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ inline void store_out(void* out, size_t idx, float x, int out_dtype) {
+  if (out_dtype == PA_F32) {
+    reinterpret_cast<float*>(out)[idx] = x;
+  } else if (out_dtype == PA_BF16) {
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(x);
+  } else {
+    reinterpret_cast<_Float16*>(out)[idx] = (_Float16)x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane helpers (wave64)
+// ---------------------------------------------------------------------------
+// DPP control codes (GCN/CDNA encoding)
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Every lane reads a lane of its own row, so bound_ctrl never matters; setting
+// it lets the compiler fold the move into the consuming add (v_add_f32_dpp).
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N lanes (N in {1,2,4,8,16,32}); every lane of a
+// group receives the group's sum.  All 64 lanes must be active.
+template <int N>
+__device__ inline float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<kDppQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp<kDppQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// raw buffer loads (SGPR descriptor + per-lane byte offset)
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Descriptor word 3 for untyped dword access on gfx9-family parts.
+constexpr int kBufferWord3 = 0x00020000;
+
+// A descriptor covering nbytes from base; accesses at or past nbytes return
+// zero without touching memory.
+__device__ inline BufRsrc make_rsrc(const void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes,
+                                           kBufferWord3);
+}
+
+__device__ inline uint4 buffer_load16(BufRsrc r, int byte_off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+}  // namespace pa

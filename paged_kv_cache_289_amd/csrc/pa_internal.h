@@ -1,0 +1,67 @@
+// Internal interface between the C-ABI host layer (pa_api.cpp) and the kernel
+// translation units.  Every launcher enqueues on the given stream and returns
+// the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "paged_attn.h"
+
+namespace pa {
+
+// Threads per workgroup of the attention kernels (four wave64s).
+#ifndef PA_WAVES
+#define PA_WAVES 4
+#endif
+constexpr int kWaves = PA_WAVES;
+constexpr int kThreads = 64 * kWaves;
+
+// Arguments of the decode / multi-query partial kernels and of the merge.
+struct AttnArgs {
+  void* out;                 // [rows][H][D], out_dtype
+  float* ws_ml;              // [rows][H][P_max][2] (running max in log2 units, sum)
+  float* ws_o;               // [rows][H][P_max][D] unnormalized partial outputs
+  const void* q;             // [rows][H][D]
+  const void* k_cache;       // [NB][Hk][B][D]
+  const void* v_cache;
+  const int32_t* block_tables;  // [S][mbs]
+  const int32_t* context_lens;  // [S]
+  const int32_t* q_offsets;     // [S+1] (multi-query only)
+  int num_heads;             // H
+  int num_kv_heads;          // Hk
+  int group;                 // G = H / Hk
+  int max_blocks_per_seq;    // mbs
+  int max_context_len;
+  int part;                  // partition length in tokens (multiple of B)
+  int max_parts;             // P_max = ceil(max_context_len / part)
+  int max_q_len;
+  int causal;
+  int out_dtype;
+  float scale_log2;          // scale * log2(e): scores are kept in log2 units
+};
+
+// Optional events recorded right around a call's main kernel (profiling aid).
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+hipError_t launch_decode(int dtype, int head_dim, int block_size, int group, int num_seqs,
+                         const AttnArgs& a, hipStream_t stream, const KernelEvents& ev);
+
+hipError_t launch_multiq(int dtype, int head_dim, int block_size, int group, int num_seqs,
+                         const AttnArgs& a, hipStream_t stream, const KernelEvents& ev);
+
+hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* token_offsets, int num_seqs, int num_kv_heads,
+                         int head_dim, int block_size, int max_blocks_per_seq,
+                         int max_blocks_used, int elem_bytes, hipStream_t stream);
+
+hipError_t launch_check(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                        int block_size, int num_blocks, int max_blocks_per_seq,
+                        int max_context_len, int32_t* bad_count, hipStream_t stream);
+
+}  // namespace pa

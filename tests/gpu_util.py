@@ -1,0 +1,109 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the library through
+its C ABI (via the ctypes binding) and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle.paged_attention as OP
+from paged_kv_cache_289_amd import workloads as W
+
+DEV = "cuda:0"
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+# Parity bar on the fp32-accumulated result: max abs error 2e-3 for bf16/fp16
+# inputs and 1e-5 for fp32 inputs.
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def ops():
+    from paged_kv_cache_289_amd import ops as _ops   # raises if the library is not built
+    return _ops
+
+
+def upload(st: W.PagedStructure, vals, device=DEV):
+    t = W.host_to_torch(vals, st.dtype, device)
+    t["block_tables"] = torch.from_numpy(st.block_tables).to(device)
+    t["context_lens"] = torch.from_numpy(st.context_lens).to(device)
+    t["q_offsets"] = torch.from_numpy(st.q_offsets).to(device)
+    return t
+
+
+def half_ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Half a unit in the last place of |x| in the output dtype (0 for fp32 output):
+    the most that rounding the exact result to that dtype can move it."""
+    if dtype == "f32":
+        return np.zeros_like(x)
+    mant = {"bf16": 7, "f16": 10}[dtype]
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    e = np.floor(np.log2(ax))
+    if dtype == "f16":
+        e = np.maximum(e, -14)
+    return 2.0 ** (e - mant - 1)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def assert_close(got: torch.Tensor, want: np.ndarray, in_dtype: str, label: str,
+                 rows=None):
+    """|got - want| <= TOL[in_dtype] (+ half an output ulp when the output is rounded
+    to bf16/fp16).  ``rows`` restricts the check to the first axis indices given."""
+    g = to_f64(got)
+    if rows is not None:
+        g, want = g[rows], want[rows]
+    out_dt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[got.dtype]
+    bound = TOL[in_dtype] + half_ulp(want, out_dt)
+    assert np.all(np.isfinite(g)), f"{label}: non-finite output"
+    err = np.abs(g - want)
+    worst = float(err.max()) if err.size else 0.0
+    excess = err - bound
+    say(f"  {label}: max|err| = {worst:.3e}  max|out| = {float(np.abs(want).max()):.3f}")
+    assert np.all(excess <= 0), (f"{label}: max abs error {worst:.3e} over the bound at "
+                                 f"{np.unravel_index(int(np.argmax(excess)), err.shape)}")
+    return worst
+
+
+def oracle_decode(st, vals, seqs=None):
+    return OP.paged_decode(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
+                           st.context_lens, st.block_size, st.scale, st.dtype, seqs=seqs)
+
+
+def oracle_multiq(st, vals, causal=True, seqs=None):
+    return OP.paged_multiq(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
+                           st.context_lens, st.q_offsets, st.block_size, st.scale, st.dtype,
+                           causal=causal, seqs=seqs)
+
+
+def run_decode(st, t, out_dtype=None, partition_tokens=0):
+    o = ops()
+    out = o.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                   st.scale, st.max_context_len, out_dtype=out_dtype,
+                   partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_multiq(st, t, causal=True, out_dtype=None, partition_tokens=0):
+    o = ops()
+    out = o.multiq(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                   t["q_offsets"], st.scale, st.max_context_len, st.max_q_len, causal=causal,
+                   out_dtype=out_dtype, partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    return out
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().to("cpu").contiguous()
+    if t.element_size() == 2:
+        return t.view(torch.int16).numpy()
+    return t.view(torch.int32).numpy()
