@@ -8,10 +8,6 @@
 
 #include "pa_internal.h"
 
-namespace pa {
-hipError_t launch_merge_rows(int head_dim, int num_seqs, const AttnArgs& a, hipStream_t st);
-}
-
 namespace {
 
 bool dtype_ok(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }

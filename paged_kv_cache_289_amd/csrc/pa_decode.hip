@@ -46,16 +46,29 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const AttnArgs
   constexpr int LPB = B / TPL;      // vector loads per block per tensor per lane
   static_assert(LPT * EPL == D && TPL * LPT == 64 && LPB * TPL == B, "layout");
 
-  const int p = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int p = blockIdx.x, g = blockIdx.y;
   const int H = a.num_heads, G = a.group;
-  const int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  // Decode: blockIdx.z is the sequence and its one query row.  Per-row mode
+  // (multi-token queries without MFMA): blockIdx.z = s * max_q_len + i is row i
+  // of sequence s, which sees the first L_s - n_s + i + 1 keys when causal.
+  int s = blockIdx.z, qrow = blockIdx.z;
+  int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  if (a.q_offsets) {
+    s = blockIdx.z / a.max_q_len;
+    const int i = blockIdx.z % a.max_q_len;
+    const int q0 = a.q_offsets[s], n = a.q_offsets[s + 1] - q0;
+    if (i >= n) return;
+    qrow = q0 + i;
+    L = min(max(a.context_lens[s], 0), a.max_context_len);
+    if (a.causal) L = max(0, min(L, L - n + i + 1));
+  }
   const int n_parts = (L + a.part - 1) / a.part;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int row = lane / LPT, col = lane % LPT;
-  const size_t head0 = (size_t)s * H + (size_t)g * G;   // first query head of the group
+  const size_t head0 = (size_t)qrow * H + (size_t)g * G;   // first query head of the group
 
   if (n_parts == 0) {  // empty context: zero output rows, written by partition 0
     if (p == 0)
@@ -304,15 +317,17 @@ __device__ inline void merge_rows(const AttnArgs& a, size_t row, int g, int n_pa
 // Separate merge launch.  Rows with a single partition were finished by the
 // partial kernel.
 template <int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(const AttnArgs a, int rows_are_queries) {
+__global__ __launch_bounds__(kThreads) void merge_kernel(const AttnArgs a) {
   const int g = blockIdx.y, s = blockIdx.z;
   size_t row = s;
-  if (rows_are_queries) {  // multi-query: blockIdx.x = row within the sequence
+  int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  if (a.q_offsets) {  // multi-token queries: blockIdx.x = row within the sequence
     const int q0 = a.q_offsets[s], n = a.q_offsets[s + 1] - q0;
-    if ((int)blockIdx.x >= n) return;
-    row = (size_t)q0 + blockIdx.x;
+    const int i = blockIdx.x;
+    if (i >= n) return;
+    row = (size_t)q0 + i;
+    if (a.causal) L = max(0, min(L, L - n + i + 1));
   }
-  const int L = min(max(a.context_lens[s], 0), a.max_context_len);
   const int n_parts = (L + a.part - 1) / a.part;
   if (n_parts <= 1) return;
   merge_rows<D>(a, row, g, n_parts);
@@ -324,14 +339,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const AttnArgs a, int r
 template <int DT, int D, int B, int GP>
 static hipError_t launch_decode_t(int num_seqs, const AttnArgs& a, hipStream_t st,
                                   const KernelEvents& ev) {
-  dim3 grid(a.max_parts, a.num_kv_heads, num_seqs);
+  // per-row mode launches one grid row per (sequence, query row) slot
+  const int rows = a.q_offsets ? num_seqs * a.max_q_len : num_seqs;
+  dim3 grid(a.max_parts, a.num_kv_heads, rows);
   if (ev.start) hipEventRecord(ev.start, st);
   hipLaunchKernelGGL((decode_partial_kernel<DT, D, B, GP>), grid, dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (ev.stop) hipEventRecord(ev.stop, st);
   if (e != hipSuccess || a.max_parts <= 1) return e;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(1, a.num_kv_heads, num_seqs), dim3(kThreads), 0, st,
-                     a, 0);
+  dim3 mgrid(a.q_offsets ? a.max_q_len : 1, a.num_kv_heads, num_seqs);
+  hipLaunchKernelGGL((merge_kernel<D>), mgrid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -369,16 +386,6 @@ hipError_t launch_decode(int dtype, int head_dim, int block_size, int group, int
     case PA_F16: return dispatch_d<PA_F16>(head_dim, block_size, group, num_seqs, a, st, ev);
     default: return dispatch_d<PA_BF16>(head_dim, block_size, group, num_seqs, a, st, ev);
   }
-}
-
-// merge used by the multi-query path (rows = query tokens)
-hipError_t launch_merge_rows(int head_dim, int num_seqs, const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.max_q_len, a.num_kv_heads, num_seqs);
-  if (head_dim == 64)
-    hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(kThreads), 0, st, a, 1);
-  else
-    hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(kThreads), 0, st, a, 1);
-  return hipGetLastError();
 }
 
 }  // namespace pa

@@ -1,0 +1,136 @@
+"""GPU parity of paged_attn_multiq (several query rows per sequence) against the fp64 oracle.
+
+Rows of a sequence are its last n positions; with the causal mask row i sees keys
+t <= L - n + i.  All calls go through the C ABI.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_289_amd import workloads as W
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def _verify_small(seed, **kw):
+    args = dict(num_seqs=5, n_new=5, ctx_lo=5, ctx_hi=400)
+    args.update(kw)
+    return W.spec_verify(seed, **args)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("part", [0, 64])
+def test_multiq_spec_verify_small(causal, part):
+    st = _verify_small(1)
+    U.say(f"multiq verify causal={causal} part={part} ctx={list(st.context_lens)}")
+    vals = W.host_values(st)
+    t = U.upload(st, vals)
+    want = U.oracle_multiq(st, vals, causal=causal)
+    for odt in (None, torch.float32):
+        out = U.run_multiq(st, t, causal=causal, out_dtype=odt, partition_tokens=part)
+        U.assert_close(out, want, "bf16", f"verify causal={causal} out={out.dtype}")
+
+
+@pytest.mark.parametrize("part", [0, 128])
+def test_multiq_chunked_prefill_small(part):
+    st = W.chunked_prefill(2, cached=300, chunk=70)
+    vals = W.host_values(st)
+    t = U.upload(st, vals)
+    out = U.run_multiq(st, t, out_dtype=torch.float32, partition_tokens=part)
+    U.assert_close(out, U.oracle_multiq(st, vals), "bf16", f"prefill part={part}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B", [8, 16, 32])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_multiq_shapes(dtype, D, B, G):
+    st = W.random_small(2000 + G * 5 + B + D, num_seqs=4, num_heads=2 * G, num_kv_heads=2,
+                        head_dim=D, block_size=B, ctx_lo=1, ctx_hi=200, q_len_max=9,
+                        dtype=dtype)
+    U.say(f"multiq {dtype} D={D} B={B} G={G} ctx={list(st.context_lens)} n={list(st.q_lens)}")
+    vals = W.host_values(st)
+    t = U.upload(st, vals)
+    want = U.oracle_multiq(st, vals)
+    for part in (0, 4 * B):
+        out = U.run_multiq(st, t, out_dtype=torch.float32, partition_tokens=part)
+        U.assert_close(out, want, dtype, f"part={part}")
+
+
+def test_multiq_with_one_row_equals_decode():
+    st = W.llama3_8b_decode(3, num_seqs=6, ctx_lo=1, ctx_hi=700)
+    vals = W.host_values(st)
+    t = U.upload(st, vals)
+    dec = U.run_decode(st, t, out_dtype=torch.float32)
+    mq = U.run_multiq(st, t, out_dtype=torch.float32)
+    want = U.oracle_decode(st, vals)
+    U.assert_close(mq, want, "bf16", "multiq n=1")
+    assert np.max(np.abs(U.to_f64(mq) - U.to_f64(dec))) <= 2e-3
+
+
+def test_multiq_row_equals_decode_on_truncated_context():
+    """Row i of a causal multi-token call equals a decode over L - n + i + 1 keys."""
+    st = _verify_small(4, num_seqs=3)
+    vals = W.host_values(st)
+    t = U.upload(st, vals)
+    mq = U.to_f64(U.run_multiq(st, t, out_dtype=torch.float32))
+    qo = st.q_offsets
+    for i in range(5):
+        ctx = np.array([int(st.context_lens[s]) - 5 + i + 1 for s in range(st.num_seqs)], np.int32)
+        sti = dataclasses.replace(st, context_lens=ctx, q_lens=np.ones(st.num_seqs, np.int32))
+        vi = dict(vals)
+        vi["q"] = vals["q"][qo[:-1] + i]
+        ti = U.upload(sti, vi)
+        dec = U.to_f64(U.run_decode(sti, ti, out_dtype=torch.float32))
+        assert np.max(np.abs(dec - mq[qo[:-1] + i])) <= 2e-3
+
+
+def test_multiq_poisoned_unused_slots_change_nothing():
+    st = _verify_small(5)
+    vals = W.host_values(st)
+    a = U.run_multiq(st, U.upload(st, vals), partition_tokens=64)
+    b = U.run_multiq(st, U.upload(st, W.poison_unused(st, vals)), partition_tokens=64)
+    assert np.all(np.isfinite(U.to_f64(b)))
+    assert np.array_equal(U.bits(a), U.bits(b))
+
+
+def test_multiq_is_deterministic():
+    st = _verify_small(6)
+    vals = W.host_values(st)
+    t = U.upload(st, vals)
+    a = U.run_multiq(st, t)
+    b = U.run_multiq(st, t)
+    assert np.array_equal(U.bits(a), U.bits(b))
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, default launch configuration, sampled rows
+# --------------------------------------------------------------------------
+
+def _full_size_multiq(st, seqs):
+    U.say(f"full size {st.name}: {st.summary()}")
+    dv = W.device_values(st, U.DEV)
+    t = dict(dv)
+    t["block_tables"] = torch.from_numpy(st.block_tables).to(U.DEV)
+    t["context_lens"] = torch.from_numpy(st.context_lens).to(U.DEV)
+    t["q_offsets"] = torch.from_numpy(st.q_offsets).to(U.DEV)
+    out = U.run_multiq(st, t)
+    out32 = U.run_multiq(st, t, out_dtype=torch.float32)
+    vals = {k: W.torch_to_host(v, st.dtype) for k, v in dv.items()}
+    want = U.oracle_multiq(st, vals, seqs=seqs)
+    rows = np.concatenate([np.arange(st.q_offsets[s], st.q_offsets[s + 1]) for s in seqs])
+    U.assert_close(out32, want, st.dtype, f"{st.name} out f32", rows=rows)
+    U.assert_close(out, want, st.dtype, f"{st.name} out {st.dtype}", rows=rows)
+
+
+def test_full_spec_verify():
+    st = W.spec_verify(0)
+    pick = {int(np.argmax(st.context_lens)), int(np.argmin(st.context_lens)), 7, 33}
+    _full_size_multiq(st, sorted(pick))
+
+
+def test_full_chunked_prefill():
+    _full_size_multiq(W.chunked_prefill(0), [0])
