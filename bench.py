@@ -226,8 +226,8 @@ def main():
     q = dv["q"]
     out = torch.empty(q.shape, dtype=q.dtype, device=dev)
     H, D = st.num_heads, st.head_dim
-    part = a.partition or ops.default_partition(st.num_seqs, st.num_kv_heads, st.block_size,
-                                                st.max_context_len, st.max_q_len)
+    part = a.partition or ops.default_partition(st.num_seqs, st.num_heads, st.num_kv_heads,
+                                                st.block_size, st.max_context_len, st.max_q_len)
     wsb = ops.workspace_size(st.num_seqs, st.total_q, st.max_q_len, H, st.num_kv_heads, D,
                              st.block_size, st.max_context_len, part)
     ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)

@@ -165,7 +165,7 @@ int paged_attn_check_inputs(const int32_t* block_tables, const int32_t* context_
 int paged_attn_set_kernel_events(void* start, void* stop);
 
 /* Partition length (tokens) that the library picks when partition_tokens is 0. */
-int paged_attn_default_partition(int num_seqs, int num_kv_heads, int block_size,
+int paged_attn_default_partition(int num_seqs, int num_heads, int num_kv_heads, int block_size,
                                  int max_context_len, int max_q_len);
 
 /* Static description of a status code. */

@@ -37,12 +37,12 @@ int check_attn_shapes(int num_seqs, int num_heads, int num_kv_heads, int head_di
   return PA_OK;
 }
 
-int resolve_partition(int partition_tokens, int num_seqs, int num_kv_heads, int block_size,
-                      int max_context_len, int max_q_len) {
+int resolve_partition(int partition_tokens, int num_seqs, int num_heads, int num_kv_heads,
+                      int block_size, int max_context_len, int max_q_len) {
   return partition_tokens > 0
              ? partition_tokens
-             : paged_attn_default_partition(num_seqs, num_kv_heads, block_size, max_context_len,
-                                            max_q_len);
+             : paged_attn_default_partition(num_seqs, num_heads, num_kv_heads, block_size,
+                                            max_context_len, max_q_len);
 }
 
 // Workspace layout: fp32 (max, sum) pairs [rows][H][P], then fp32 partial
@@ -86,12 +86,22 @@ const char* paged_attn_status_string(int status) {
   }
 }
 
-int paged_attn_default_partition(int num_seqs, int num_kv_heads, int block_size,
+int paged_attn_default_partition(int num_seqs, int num_heads, int num_kv_heads, int block_size,
                                  int max_context_len, int max_q_len) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  (void)max_context_len;
-  int part = max_q_len > 1 ? 512 : 2048;
+  int part;
+  if (max_q_len > 1) {
+    // multi-token queries: one workgroup per (32-row tile, KV head, sequence,
+    // partition); size partitions so that about 2048 workgroups cover the
+    // longest context, in 32-token tiles, between 256 and 4096 tokens
+    const int group = num_kv_heads > 0 ? std::max(1, num_heads / num_kv_heads) : 1;
+    const int64_t units = (int64_t)std::max(1, num_seqs) * std::max(1, num_kv_heads) *
+                          ceil_div(max_q_len * group, 32);
+    int64_t want = (int64_t)max_context_len * units / 2048;
+    want = std::min<int64_t>(4096, std::max<int64_t>(256, want));
+    part = (int)((want + 31) / 32 * 32);
+  } else {
+    part = 2048;
+  }
   if (part % block_size) part = ceil_div(part, block_size) * block_size;
   return part;
 }
@@ -103,8 +113,8 @@ size_t paged_attn_workspace_size(int num_seqs, int total_q, int max_q_len, int n
       head_dim < 1 || block_size < 1 || max_context_len < 0 || partition_tokens < 0)
     return 0;
   if (partition_tokens > 0 && partition_tokens % block_size) return 0;
-  const int part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, block_size,
-                                     max_context_len, max_q_len);
+  const int part = resolve_partition(partition_tokens, num_seqs, num_heads, num_kv_heads,
+                                     block_size, max_context_len, max_q_len);
   const int max_parts = ceil_div(max_context_len, part);
   return workspace_bytes_for(total_q, num_seqs, num_heads, num_kv_heads, head_dim, max_parts);
 }
@@ -123,8 +133,8 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
 
-  const int part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, block_size,
-                                     max_context_len, 1);
+  const int part = resolve_partition(partition_tokens, num_seqs, num_heads, num_kv_heads,
+                                     block_size, max_context_len, 1);
   const int max_parts = std::max(1, ceil_div(max_context_len, part));
   const size_t need =
       workspace_bytes_for(num_seqs, num_seqs, num_heads, num_kv_heads, head_dim, max_parts);
@@ -174,8 +184,8 @@ int paged_attn_multiq(void* out, const void* q, const void* k_cache, const void*
     return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
 
-  const int part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, block_size,
-                                     max_context_len, max_q_len);
+  const int part = resolve_partition(partition_tokens, num_seqs, num_heads, num_kv_heads,
+                                     block_size, max_context_len, max_q_len);
   const int max_parts = std::max(1, ceil_div(max_context_len, part));
   const int rows = total_q;
   const size_t need =

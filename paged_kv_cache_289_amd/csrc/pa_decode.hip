@@ -336,6 +336,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const AttnArgs a) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
+// Merge launch shared with the multi-query kernel (rows = query tokens).
+hipError_t launch_merge(int head_dim, int num_seqs, const AttnArgs& a, hipStream_t st) {
+  dim3 mgrid(a.q_offsets ? a.max_q_len : 1, a.num_kv_heads, num_seqs);
+  if (head_dim == 64)
+    hipLaunchKernelGGL((merge_kernel<64>), mgrid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<128>), mgrid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int DT, int D, int B, int GP>
 static hipError_t launch_decode_t(int num_seqs, const AttnArgs& a, hipStream_t st,
                                   const KernelEvents& ev) {
@@ -347,9 +357,7 @@ static hipError_t launch_decode_t(int num_seqs, const AttnArgs& a, hipStream_t s
   hipError_t e = hipGetLastError();
   if (ev.stop) hipEventRecord(ev.stop, st);
   if (e != hipSuccess || a.max_parts <= 1) return e;
-  dim3 mgrid(a.q_offsets ? a.max_q_len : 1, a.num_kv_heads, num_seqs);
-  hipLaunchKernelGGL((merge_kernel<D>), mgrid, dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  return launch_merge(D, num_seqs, a, st);
 }
 
 template <int DT, int D, int B>

@@ -3,14 +3,321 @@
 // paragraph) and prefill chunks ("Local_LLM_03_vLLM_Architecture",
 // chunked-prefill slide).  The n query rows of a sequence are its last n
 // positions; with the causal mask row i sees keys t <= L - n + i.
+//
+// bf16/f16: matrix-core kernel.  For one KV head g of sequence s, the query
+// rows are the n*G pairs (i, h) of the group (row r = i*G + h), tiled by 32.
+// Each wave owns one 32-row tile and walks 32-token K/V tiles of a context
+// partition with v_mfma_f32_32x32x16 (fp32 accumulation):
+//
+//   S^T = K Q^T      A = K tile (token x dims), B = Q^T; in the result lane l
+//                    holds 16 of the 32 tokens of row m = l % 32, so the row's
+//                    softmax max/sum is 16 in-lane steps plus one exchange
+//                    with lane l ^ 32.
+//   V^T = V I        the same 32x32 layout applied to V times an identity:
+//                    lane l receives V at dim 32b + l % 32 for exactly the
+//                    tokens whose probabilities it holds, in the same order.
+//   O^T += V^T P^T   A = V^T and B = P^T come straight out of those registers
+//                    (rounded to the input dtype), so nothing moves between
+//                    lanes or through LDS inside the loop.
+//
+// The four waves of a workgroup split the partition's tiles; their (max, sum,
+// O) states are merged through LDS, then written as the final output or as a
+// partition partial for merge_kernel.  fp32: every query row runs the decode
+// kernel over its own visible length.
 #include "pa_common.h"
 
 namespace pa {
 
-// Vector-ALU path: every query row runs the decode kernel over its own visible
-// length (per-row mode of launch_decode).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int DT> struct Mma;
+
+template <> struct Mma<PA_BF16> {
+  static constexpr uint32_t kOne = 0x3F80u;   // 1.0
+  __device__ static inline f32x16_t mma(const uint4& a, const uint4& b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  // two floats -> two bf16 (round to nearest even), lo in the low half
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+  }
+};
+
+template <> struct Mma<PA_F16> {
+  static constexpr uint32_t kOne = 0x3C00u;   // 1.0
+  __device__ static inline f32x16_t mma(const uint4& a, const uint4& b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+};
+
+// x rounded to the nearest bf16, as a float
+__device__ inline float bf16_round(float x) {
+  return __uint_as_float((uint32_t)f32_to_bf16_rne(x) << 16);
+}
+
+template <int DT>
+__device__ inline uint4 pack8(const f32x16_t& x, int base) {
+  using M = Mma<DT>;
+  return make_uint4(M::pack2(x[base + 0], x[base + 1]), M::pack2(x[base + 2], x[base + 3]),
+                    M::pack2(x[base + 4], x[base + 5]), M::pack2(x[base + 6], x[base + 7]));
+}
+
+// token offset (within a 32-token tile) of C-layout register v in lane half hh
+__device__ constexpr int tile_token(int v, int hh) { return 8 * (v / 4) + 4 * hh + (v % 4); }
+
+template <int DT, int D, int B>
+__global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a) {
+  using M = Mma<DT>;
+  constexpr int KS = D / 16;   // k-steps of QK over head_dim
+  constexpr int DB = D / 32;   // 32-dim blocks of the output
+  constexpr int kElem = 2;
+
+  const int G = a.group, H = a.num_heads, Hk = a.num_kv_heads;
+  const int g = blockIdx.y, s = blockIdx.z;
+  const int rt_count = (a.max_q_len * G + 31) / 32;
+  const int rt = blockIdx.x % rt_count, p = blockIdx.x / rt_count;
+  const int q0 = a.q_offsets[s], n = a.q_offsets[s + 1] - q0;
+  const int n_rows = n * G;
+  if (rt * 32 >= n_rows) return;
+  const int L = min(max(a.context_lens[s], 0), a.max_context_len);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5;            // lane half: which 16 of a tile's 32 tokens
+  const int mcol = lane & 31;          // this lane's query row within the tile
+  const int r = rt * 32 + mcol;
+  const bool row_ok = r < n_rows;
+  const int qi = row_ok ? r / G : 0;   // query token of the row
+  const int qh = row_ok ? r % G : 0;   // head within the group
+  // visible keys of this row, and of the tile's last (most-seeing) row
+  const int lrow = !row_ok ? 0 : (a.causal ? max(0, min(L, L - n + qi + 1)) : L);
+  const int last_i = (min(rt * 32 + 31, n_rows - 1)) / G;
+  const int first_i = (rt * 32) / G;
+  const int l_tile_max = a.causal ? max(0, min(L, L - n + last_i + 1)) : L;
+  const int l_tile_min = a.causal ? max(0, min(L, L - n + first_i + 1)) : L;
+  const int parts_row = (lrow + a.part - 1) / a.part;
+  const size_t out_row = ((size_t)(q0 + qi) * H + (size_t)g * G + qh);   // (token, head) index
+
+  const int tok0 = p * a.part;
+  if (L == 0) {  // nothing visible: zero rows, written once
+    if (p == 0 && wave == 0 && row_ok)
+      for (int d = hh * (D / 2); d < (hh + 1) * (D / 2); ++d) store_out(a.out, out_row * D + d, 0.f, a.out_dtype);
+    return;
+  }
+  if (tok0 >= l_tile_max) return;      // no row of this tile sees this partition
+  const int tok_end = min(tok0 + a.part, l_tile_max);
+  const int lim = min(lrow, tok_end);  // this lane-row's keys end here (within the partition)
+
+  // Q^T operand: row m = lane % 32, dims 16 ks + 8 hh .. +7
+  uint4 qv[KS];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q) + (out_row * D + hh * 8) / 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qv[ks] = row_ok ? qp[2 * ks] : make_uint4(0, 0, 0, 0);
+  }
+  // identity operands selecting dims 0..15 and 16..31 of a 32-dim block
+  uint4 eye[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j2 = 0; j2 < 4; ++j2) {
+      const int k0 = hh * 8 + 2 * j2 + 16 * kk;
+      w[j2] = (k0 == mcol ? M::kOne : 0u) | ((k0 + 1 == mcol ? M::kOne : 0u) << 16);
+    }
+    eye[kk] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+
+  f32x16_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+  float m_run = kNegInf, l_run = 0.f;
+
+  const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  const char* kbase = static_cast<const char*>(a.k_cache);
+  const char* vbase = static_cast<const char*>(a.v_cache);
+  const size_t row_bytes = (size_t)D * kElem;
+
+  for (int t0 = tok0 + 32 * wave; t0 < tok_end; t0 += 32 * kWaves) {
+    // this lane loads token t0 + mcol (clamped into the valid range: slots at
+    // or beyond L may hold anything), dims 16 ks + 8 hh .. +7
+    const int t = min(t0 + mcol, L - 1);
+    const int phys = tbl[t / B];
+    const size_t roff = (((size_t)phys * Hk + g) * B + (t % B)) * row_bytes + hh * 16;
+    const uint4* kp = reinterpret_cast<const uint4*>(kbase + roff);
+    const uint4* vp = reinterpret_cast<const uint4*>(vbase + roff);
+    uint4 kr[KS], vr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kr[ks] = kp[2 * ks];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) vr[ks] = vp[2 * ks];
+
+    // S^T = K Q^T: lane holds tokens t0 + tile_token(v, hh) of its row
+    f32x16_t sc = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sc = M::mma(kr[ks], qv[ks], sc);
+
+    float mx = kNegInf;
+    if (t0 + 32 <= min(l_tile_min, tok_end)) {   // wave-uniform: no key of the tile is masked
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sc[v] *= a.scale_log2;
+        mx = fmaxf(mx, sc[v]);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sc[v] = (t0 + tile_token(v, hh) < lim) ? sc[v] * a.scale_log2 : kNegInf;
+        mx = fmaxf(mx, sc[v]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float ms = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - ms);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      sc[v] = fast_exp2(sc[v] - ms);
+      psum += sc[v];
+    }
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = __builtin_fmaf(l_run, alpha, psum);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+
+    // P^T operands.  bf16 keeps 8 significant bits, too few for the
+    // probabilities at short contexts, so P is split into a bf16 head and a bf16
+    // residual (p = hi + lo to about 2^-17) and both are multiplied; f16's 11
+    // bits are used as they are.
+    const uint4 pb0 = pack8<DT>(sc, 0), pb1 = pack8<DT>(sc, 8);
+    uint4 pl0, pl1;
+    if constexpr (DT == PA_BF16) {
+      f32x16_t res;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) res[v] = sc[v] - bf16_round(sc[v]);
+      pl0 = pack8<DT>(res, 0);
+      pl1 = pack8<DT>(res, 8);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      f32x16_t vt = M::mma(vr[2 * db], eye[0], f32x16_t{});
+      vt = M::mma(vr[2 * db + 1], eye[1], vt);
+      const uint4 va0 = pack8<DT>(vt, 0), va1 = pack8<DT>(vt, 8);
+      o[db] = M::mma(va0, pb0, o[db]);
+      o[db] = M::mma(va1, pb1, o[db]);
+      if constexpr (DT == PA_BF16) {
+        o[db] = M::mma(va0, pl0, o[db]);
+        o[db] = M::mma(va1, pl1, o[db]);
+      }
+    }
+  }
+
+  // merge the waves' states through LDS, one wave at a time, into wave 0
+  __shared__ float sm_o[32][D + 4];
+  __shared__ float sm_m[32], sm_l[32];
+  for (int w = 1; w < kWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sm_o[mcol][32 * db + tile_token(v, hh)] = o[db][v];
+      if (hh == 0) {
+        sm_m[mcol] = m_run;
+        sm_l[mcol] = l_run;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const float m2 = sm_m[mcol], l2 = sm_l[mcol];
+      const float mxw = fmaxf(m_run, m2);
+      const float ms = (mxw == kNegInf) ? 0.f : mxw;
+      const float a1 = fast_exp2(m_run - ms), a2 = fast_exp2(m2 - ms);
+      l_run = l_run * a1 + l2 * a2;
+      m_run = mxw;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          o[db][v] = o[db][v] * a1 + sm_o[mcol][32 * db + tile_token(v, hh)] * a2;
+    }
+    __syncthreads();
+  }
+  if (wave != 0 || !row_ok) return;
+
+  // lane (mcol, hh) holds dims 32 db + 8 c + 4 hh + (0..3) of its row
+  if (parts_row <= 1) {
+    if (p != 0) return;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        store_out(a.out, out_row * D + 32 * db + tile_token(v, hh), o[db][v] * inv, a.out_dtype);
+  } else if (p < parts_row) {
+    const size_t slot = out_row * a.max_parts + p;
+    float* po = a.ws_o + slot * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * c + 4 * hh) =
+            make_float4(o[db][4 * c], o[db][4 * c + 1], o[db][4 * c + 2], o[db][4 * c + 3]);
+    if (hh == 0) {
+      a.ws_ml[2 * slot] = m_run;
+      a.ws_ml[2 * slot + 1] = l_run;
+    }
+  }
+}
+
+hipError_t launch_merge(int head_dim, int num_seqs, const AttnArgs& a, hipStream_t st);
+
+template <int DT, int D, int B>
+static hipError_t launch_mfma_t(int num_seqs, const AttnArgs& a, hipStream_t st,
+                                const KernelEvents& ev) {
+  const int rt_count = (a.max_q_len * a.group + 31) / 32;
+  dim3 grid(rt_count * a.max_parts, a.num_kv_heads, num_seqs);
+  if (ev.start) hipEventRecord(ev.start, st);
+  hipLaunchKernelGGL((multiq_mfma_kernel<DT, D, B>), grid, dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (ev.stop) hipEventRecord(ev.stop, st);
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  return launch_merge(D, num_seqs, a, st);
+}
+
+template <int DT, int D>
+static hipError_t dispatch_mfma_b(int block_size, int num_seqs, const AttnArgs& a,
+                                  hipStream_t st, const KernelEvents& ev) {
+  switch (block_size) {
+    case 8: return launch_mfma_t<DT, D, 8>(num_seqs, a, st, ev);
+    case 16: return launch_mfma_t<DT, D, 16>(num_seqs, a, st, ev);
+    default: return launch_mfma_t<DT, D, 32>(num_seqs, a, st, ev);
+  }
+}
+
+template <int DT>
+static hipError_t dispatch_mfma(int head_dim, int block_size, int num_seqs, const AttnArgs& a,
+                                hipStream_t st, const KernelEvents& ev) {
+  if (head_dim == 64) return dispatch_mfma_b<DT, 64>(block_size, num_seqs, a, st, ev);
+  return dispatch_mfma_b<DT, 128>(block_size, num_seqs, a, st, ev);
+}
+
 hipError_t launch_multiq(int dtype, int head_dim, int block_size, int group, int num_seqs,
                          const AttnArgs& a, hipStream_t st, const KernelEvents& ev) {
+  if (dtype == PA_BF16) return dispatch_mfma<PA_BF16>(head_dim, block_size, num_seqs, a, st, ev);
+  if (dtype == PA_F16) return dispatch_mfma<PA_F16>(head_dim, block_size, num_seqs, a, st, ev);
+  // fp32: vector-ALU path, each query row as a decode row over its visible length
   return launch_decode(dtype, head_dim, block_size, group, num_seqs, a, st, ev);
 }
 

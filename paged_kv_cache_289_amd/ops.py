@@ -32,7 +32,7 @@ SIGNATURES = {
                                _I, _F, _I, _I, _I, _I, _P, _Z, _P]),
     "paged_kv_gather": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "paged_attn_check_inputs": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
-    "paged_attn_default_partition": (_I, [_I, _I, _I, _I, _I]),
+    "paged_attn_default_partition": (_I, [_I, _I, _I, _I, _I, _I]),
     "paged_attn_set_kernel_events": (_I, [_P, _P]),
     "paged_attn_status_string": (ctypes.c_char_p, [_I]),
 }
@@ -93,9 +93,10 @@ def _need_contig(**ts):
             raise PagedAttnError(n, PA_ERR_SHAPE, f"{n} must be contiguous")
 
 
-def default_partition(num_seqs, num_kv_heads, block_size, max_context_len, max_q_len=1) -> int:
-    return LIB.paged_attn_default_partition(num_seqs, num_kv_heads, block_size, max_context_len,
-                                            max_q_len)
+def default_partition(num_seqs, num_heads, num_kv_heads, block_size, max_context_len,
+                      max_q_len=1) -> int:
+    return LIB.paged_attn_default_partition(num_seqs, num_heads, num_kv_heads, block_size,
+                                            max_context_len, max_q_len)
 
 
 def workspace_size(num_seqs, total_q, max_q_len, num_heads, num_kv_heads, head_dim, block_size,

@@ -115,4 +115,5 @@ def test_workspace_size_formula():
     assert n == 64 * 32 * 16 * 130 * 4
     assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 256, 256) == 0     # one partition
     assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 24) == 0     # rejected
-    assert ops.default_partition(64, 8, 16, 4096, 1) % 16 == 0
+    assert ops.default_partition(64, 32, 8, 16, 4096, 1) % 16 == 0
+    assert ops.default_partition(1, 32, 8, 16, 4608, 512) % 32 == 0
