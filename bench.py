@@ -226,8 +226,12 @@ def main():
     q = dv["q"]
     out = torch.empty(q.shape, dtype=q.dtype, device=dev)
     H, D = st.num_heads, st.head_dim
-    part = a.partition or ops.default_partition(st.num_seqs, st.num_heads, st.num_kv_heads,
-                                                st.block_size, st.max_context_len, st.max_q_len)
+    # 0 = the library's choice: balanced split for decode, a partition size for
+    # multi-token queries (reported below)
+    part = a.partition
+    part_used = part or (ops.default_partition(st.num_seqs, st.num_heads, st.num_kv_heads,
+                                               st.block_size, st.max_context_len, st.max_q_len)
+                         if is_multiq else "balanced split")
     wsb = ops.workspace_size(st.num_seqs, st.total_q, st.max_q_len, H, st.num_kv_heads, D,
                              st.block_size, st.max_context_len, part)
     ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
@@ -293,7 +297,7 @@ def main():
             "workload": st.name, "num_seqs": st.num_seqs, "num_heads": H,
             "num_kv_heads": st.num_kv_heads, "head_dim": D, "block_size": st.block_size,
             "sum_context": int(st.context_lens.sum()), "max_context": st.max_context_len,
-            "query_tokens": st.total_q, "layers": layers, "partition_tokens": part,
+            "query_tokens": st.total_q, "layers": layers, "partition_tokens": part_used,
             "pool_replicas": reps if layers == 1 else layers, "seed": a.seed,
             "pool_blocks": st.num_blocks,
         },
@@ -327,7 +331,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBPS, 4)}
     roof["traffic"] = measured_traffic(st.name, res["source_hash"])
-    roof["kernel"] = "multi-query main kernel" if is_multiq else "decode partial kernel"
+    roof["kernel"] = "multi-query main kernel" if is_multiq else "decode split kernel"
     roof["algorithmic_bytes_per_launch"] = int(basis) if basis is not None else None
     if is_multiq:
         res["tflops"] = round(flops_of(st) / (call_ms * 1e-3) / 1e12, 2)

@@ -71,9 +71,12 @@ typedef void* pa_stream_t;
  * Bytes of device workspace that paged_attn_decode (total_q == num_seqs,
  * max_q_len == 1) or paged_attn_multiq needs for these shapes when called
  * with the same partition_tokens (0 = the library's choice).  The workspace
- * holds fp32 (max, sum, unnormalized output) partials of each context
- * partition for the log-sum-exp merge.  0 is a legal answer (no merge
- * needed).  Returns 0 as well for arguments the entry points would reject.
+ * holds the work plan and the fp32 (max, sum, unnormalized output) partials of
+ * the context pieces that the log-sum-exp merge combines; its contents need no
+ * initialization and are overwritten by every call (so calls that run
+ * concurrently need separate workspaces).  0 is a legal answer (no merge
+ * needed; only for multi-token calls whose contexts fit one partition).
+ * Returns 0 as well for arguments the entry points would reject.
  */
 size_t paged_attn_workspace_size(int num_seqs, int total_q, int max_q_len, int num_heads,
                                  int num_kv_heads, int head_dim, int block_size,
@@ -87,10 +90,11 @@ size_t paged_attn_workspace_size(int num_seqs, int total_q, int max_q_len, int n
  * context_lens[s] keys of KV head h / G of sequence s, gathered through the
  * block table (the decode step's attention over every prior token,
  * "Local_LLM_03_vLLM_Architecture", KV-cache and PagedAttention slides).
- * Long contexts are split into partitions of partition_tokens tokens
- * (0 = library's choice; otherwise a positive multiple of block_size) whose
- * partial results are merged by log-sum-exp in a second kernel.
- * workspace may be NULL when paged_attn_workspace_size() returns 0.
+ * The (sequence, KV head, block) items are cut into equal pieces, one per
+ * resident wave; pieces of one context are merged by log-sum-exp in a second
+ * kernel.  partition_tokens = 0 lets the library size the pieces; a positive
+ * multiple of block_size fixes each piece at that many tokens.  Batches of
+ * more than 8192 sequences use fixed context partitions instead.
  */
 int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens,
@@ -164,7 +168,9 @@ int paged_attn_check_inputs(const int32_t* block_tables, const int32_t* context_
  */
 int paged_attn_set_kernel_events(void* start, void* stop);
 
-/* Partition length (tokens) that the library picks when partition_tokens is 0. */
+/* Partition length (tokens) that the library picks when partition_tokens is 0
+   for multi-token queries, or for decode batches above 8192 sequences (other
+   decode calls use the balanced split and no fixed partition). */
 int paged_attn_default_partition(int num_seqs, int num_heads, int num_kv_heads, int block_size,
                                  int max_context_len, int max_q_len);
 

@@ -45,22 +45,94 @@ int resolve_partition(int partition_tokens, int num_seqs, int num_heads, int num
                                             max_context_len, max_q_len);
 }
 
-// Workspace layout: fp32 (max, sum) pairs [rows][H][P], then fp32 partial
-// outputs [rows][H][P][D].
-size_t workspace_bytes_for(int rows, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                           int max_parts) {
+// Partition-mode workspace: fp32 (max, sum) pairs [rows][H][P], then fp32
+// partial outputs [rows][H][P][D].
+size_t workspace_bytes_for(int rows, int num_heads, int head_dim, int max_parts) {
   if (max_parts <= 1) return 0;
-  (void)num_seqs;
-  (void)num_kv_heads;
   return (size_t)rows * num_heads * max_parts * ((size_t)head_dim + 2) * sizeof(float);
 }
 
-void split_workspace(void* ws, int rows, int num_heads, int max_parts, int head_dim,
-                     pa::AttnArgs* a) {
+void split_workspace(void* ws, int rows, int num_heads, int max_parts, pa::AttnArgs* a) {
   float* base = static_cast<float*>(ws);
   a->ws_ml = base;
   a->ws_o = base + (size_t)rows * num_heads * max_parts * 2;
-  (void)head_dim;
+}
+
+// Balanced-split decode plan.  Work items are (sequence, KV head, block);
+// `bound` is the most there can be.  With partition_tokens > 0 every wave takes
+// partition_tokens / B blocks; otherwise the launch is the resident wave count
+// and the device splits the items evenly.
+struct SplitPlan {
+  bool use = false;
+  int chunk = 0;          // 0: decided on the device
+  int waves = 0;          // waves launched (multiple of kWaves)
+  int workgroups = 0;
+};
+
+int64_t split_bound(int num_seqs, int num_kv_heads, int block_size, int max_context_len) {
+  return (int64_t)num_seqs * num_kv_heads * ceil_div(max_context_len, block_size);
+}
+
+SplitPlan plan_split(int num_seqs, int num_kv_heads, int block_size, int max_context_len,
+                     int partition_tokens, int resident_waves) {
+  SplitPlan p;
+  if (num_seqs > pa::kMaxSplitSeqs) return p;
+  p.use = true;
+  const int64_t bound = split_bound(num_seqs, num_kv_heads, block_size, max_context_len);
+  int64_t waves;
+  if (partition_tokens > 0) {
+    p.chunk = partition_tokens / block_size;
+    waves = (bound + p.chunk - 1) / p.chunk;
+  } else {
+    waves = std::min<int64_t>(bound, std::min(resident_waves, pa::kMaxSplitWaves));
+  }
+  waves = std::max<int64_t>(1, waves);
+  p.workgroups = (int)((waves + pa::kWaves - 1) / pa::kWaves);
+  p.waves = p.workgroups * pa::kWaves;
+  return p;
+}
+
+// Split-mode workspace: int plan [2 + S + 1] (16-byte aligned), then fp32
+// (max, sum) pairs and fp32 partial outputs for (S Hk + waves) slots x G heads.
+size_t split_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                             int waves) {
+  const size_t plan = ((size_t)(3 + num_seqs) * sizeof(int) + 15) / 16 * 16;
+  const size_t slots = (size_t)num_seqs * num_kv_heads + waves;
+  const size_t group = (size_t)(num_heads / num_kv_heads);
+  return plan + slots * group * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+void split_workspace_ptrs(void* ws, int num_seqs, int num_heads, int num_kv_heads, int waves,
+                          pa::AttnArgs* a) {
+  const size_t plan = ((size_t)(3 + num_seqs) * sizeof(int) + 15) / 16 * 16;
+  const size_t slots = (size_t)num_seqs * num_kv_heads + waves;
+  const size_t group = (size_t)(num_heads / num_kv_heads);
+  a->plan = static_cast<int*>(ws);
+  a->ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + plan);
+  a->ws_o = a->ws_ml + slots * group * 2;
+}
+
+// Waves the workspace must allow for when the launch size is not known yet
+// (it depends on the device's CU count and the kernel's occupancy).
+int split_waves_bound(int num_seqs, int num_kv_heads, int block_size, int max_context_len,
+                      int partition_tokens) {
+  return plan_split(num_seqs, num_kv_heads, block_size, max_context_len, partition_tokens,
+                    pa::kMaxSplitWaves).waves;
+}
+
+// CUs of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 }  // namespace
@@ -113,10 +185,17 @@ size_t paged_attn_workspace_size(int num_seqs, int total_q, int max_q_len, int n
       head_dim < 1 || block_size < 1 || max_context_len < 0 || partition_tokens < 0)
     return 0;
   if (partition_tokens > 0 && partition_tokens % block_size) return 0;
+  if (num_heads % num_kv_heads) return 0;
+  if (max_q_len <= 1 && num_seqs <= pa::kMaxSplitSeqs) {   // balanced-split decode
+    if (num_seqs == 0) return 0;
+    const int waves = split_waves_bound(num_seqs, num_kv_heads, block_size, max_context_len,
+                                        partition_tokens);
+    return split_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, waves);
+  }
   const int part = resolve_partition(partition_tokens, num_seqs, num_heads, num_kv_heads,
                                      block_size, max_context_len, max_q_len);
   const int max_parts = ceil_div(max_context_len, part);
-  return workspace_bytes_for(total_q, num_seqs, num_heads, num_kv_heads, head_dim, max_parts);
+  return workspace_bytes_for(total_q, num_heads, head_dim, max_parts);
 }
 
 int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -133,34 +212,56 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
 
-  const int part = resolve_partition(partition_tokens, num_seqs, num_heads, num_kv_heads,
-                                     block_size, max_context_len, 1);
-  const int max_parts = std::max(1, ceil_div(max_context_len, part));
-  const size_t need =
-      workspace_bytes_for(num_seqs, num_seqs, num_heads, num_kv_heads, head_dim, max_parts);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-    return PA_ERR_WORKSPACE;
-
   pa::AttnArgs a{};
   a.out = out;
-  if (need > 0) split_workspace(workspace, num_seqs, num_heads, max_parts, head_dim, &a);
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.q_offsets = nullptr;
+  a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = num_heads / num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
-  a.part = part;
-  a.max_parts = max_parts;
   a.max_q_len = 1;
   a.causal = 0;
   a.out_dtype = out_dtype;
   a.scale_log2 = scale * 1.4426950408889634f;
+
+  if (num_seqs <= pa::kMaxSplitSeqs) {
+    // the workspace is checked against the device-independent bound (what
+    // paged_attn_workspace_size returns) before any HIP call
+    const int bound_waves = split_waves_bound(num_seqs, num_kv_heads, block_size,
+                                              max_context_len, partition_tokens);
+    const size_t need = split_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                              bound_waves);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
+    // balanced split over the resident waves of this device
+    const int wgs = pa::split_workgroups_per_cu(dtype, head_dim, block_size, a.group);
+    const int resident = std::min(pa::kMaxSplitWaves,
+                                  device_cus() * wgs * pa::kWaves);
+    const SplitPlan sp = plan_split(num_seqs, num_kv_heads, block_size, max_context_len,
+                                    partition_tokens, resident);
+    split_workspace_ptrs(workspace, num_seqs, num_heads, num_kv_heads, sp.waves, &a);
+    a.chunk_blocks = sp.chunk;
+    a.split_workgroups = sp.workgroups;
+    a.part = 0;
+    a.max_parts = 0;
+  } else {
+    const int part = resolve_partition(partition_tokens, num_seqs, num_heads, num_kv_heads,
+                                       block_size, max_context_len, 1);
+    const int max_parts = std::max(1, ceil_div(max_context_len, part));
+    const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, max_parts);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+      return PA_ERR_WORKSPACE;
+    if (need > 0) split_workspace(workspace, num_seqs, num_heads, max_parts, &a);
+    a.part = part;
+    a.max_parts = max_parts;
+    a.plan = nullptr;
+  }
   hipError_t e = pa::launch_decode(dtype, head_dim, block_size, a.group, num_seqs, a,
                                    static_cast<hipStream_t>(stream), t_events);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -188,14 +289,15 @@ int paged_attn_multiq(void* out, const void* q, const void* k_cache, const void*
                                      block_size, max_context_len, max_q_len);
   const int max_parts = std::max(1, ceil_div(max_context_len, part));
   const int rows = total_q;
-  const size_t need =
-      workspace_bytes_for(rows, num_seqs, num_heads, num_kv_heads, head_dim, max_parts);
+  const size_t need = workspace_bytes_for(rows, num_heads, head_dim, max_parts);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PA_ERR_WORKSPACE;
 
   pa::AttnArgs a{};
   a.out = out;
-  if (need > 0) split_workspace(workspace, rows, num_heads, max_parts, head_dim, &a);
+  if (need > 0) split_workspace(workspace, rows, num_heads, max_parts, &a);
+  a.num_seqs = num_seqs;
+  a.plan = nullptr;
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;

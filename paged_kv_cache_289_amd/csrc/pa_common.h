@@ -135,6 +135,20 @@ __device__ inline float group_sum(float x) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 and leaves the
+// export and LDS/scalar counters unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// ---------------------------------------------------------------------------
+// read-only metadata through the constant address space
+// ---------------------------------------------------------------------------
+// Block tables and context lengths are never written while a kernel runs;
+// reading them through an address-space-4 pointer lets the compiler use scalar
+// loads for wave-uniform indices even in kernels that store elsewhere.
+typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+
+__device__ inline ConstI32Ptr as_const(const int32_t* p) { return (ConstI32Ptr)p; }
+
 // ---------------------------------------------------------------------------
 // raw buffer loads (SGPR descriptor + per-lane byte offset)
 // ---------------------------------------------------------------------------

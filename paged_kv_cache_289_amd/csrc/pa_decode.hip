@@ -2,9 +2,8 @@
 //
 // The cache is read through each sequence's block table of physical block ids
 // (the PagedAttention kernel that gathers K/V from scattered blocks,
-// "Local_LLM_03_vLLM_Architecture", PagedAttention slide).  One workgroup owns
-// one (partition of the context, KV head, sequence); all G query heads of the
-// KV head's group are served from the same K/V bytes (GQA-8 in the slide's
+// "Local_LLM_03_vLLM_Architecture", PagedAttention slide).  All G query heads of
+// a KV head's group are served from the same K/V bytes (GQA-8 in the slide's
 // KV sizing), so every K/V byte is read from HBM once.
 //
 // Lane layout (wave64).  A token's head_dim row of one KV head is D*elem
@@ -16,13 +15,19 @@
 // Per block: QK partial dots (bf16/f16 dot2, fp32 FMA for f32) on the lane's
 // 16 bytes, a DPP all-reduce over the LPT lanes of the token, online softmax in
 // base 2 (scores pre-multiplied by scale*log2 e), and PV accumulated in fp32 on
-// the same lanes, which already hold that token's V dims.  The next block's
-// K/V loads are issued before the current block is computed.
+// the same lanes, which already hold that token's V dims.
 //
-// Epilogue: the TPL token rows of a wave, then the four waves, are merged by
-// log-sum-exp; a sequence whose context fits one partition writes the final
-// output, otherwise the partition's (max, sum, unnormalized output) goes to
-// the workspace and merge_kernel combines the partitions.
+// Two ways to cut the work into waves:
+//  * split (decode default): every (sequence, KV head, block) item is numbered
+//    in one list and each resident wave takes an equal contiguous chunk, so all
+//    waves finish together whatever the mix of context lengths.  A chunk that
+//    covers a whole (sequence, KV head) writes the output; pieces of a longer
+//    one write (max, sum, unnormalized output) partials that split_merge_kernel
+//    combines by log-sum-exp.
+//  * partitions (multi-token fp32 rows, very large batches): one workgroup per
+//    (context partition, KV head, row); its four waves interleave the
+//    partition's blocks and merge through LDS; merge_kernel combines
+//    partitions.
 #include <type_traits>
 
 #include "pa_common.h"
@@ -34,41 +39,376 @@ namespace pa {
 #endif
 constexpr int NBUF = PA_NBUF;   // register ring depth: blocks in flight per wave + 1
 
-template <int D>
-__device__ inline void merge_rows(const AttnArgs& a, size_t row, int g, int n_parts);
-
+// ---------------------------------------------------------------------------
+// one wave's walk over some blocks of one (row, KV head)
+// ---------------------------------------------------------------------------
 template <int DT, int D, int B, int GP>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const AttnArgs a) {
+struct DecodeWave {
   using E = Elem<DT>;
-  constexpr int EPL = E::kPerVec;   // elements per lane per token
-  constexpr int LPT = D / EPL;      // lanes per token row
-  constexpr int TPL = 64 / LPT;     // token rows per wave
-  constexpr int LPB = B / TPL;      // vector loads per block per tensor per lane
+  static constexpr int EPL = E::kPerVec;   // elements per lane per token
+  static constexpr int LPT = D / EPL;      // lanes per token row
+  static constexpr int TPL = 64 / LPT;     // token rows per wave
+  static constexpr int LPB = B / TPL;      // vector loads per block per tensor per lane
+  static constexpr int kRowBytes = D * E::kBytes;
+  static constexpr int kSliceBytes = B * kRowBytes;   // one (block, KV head) slice
   static_assert(LPT * EPL == D && TPL * LPT == 64 && LPB * TPL == B, "layout");
 
+  int row, col;                 // token row within a load, 16-byte column
+  uint4 qv[GP];
+  float m[GP], l[GP], o[GP][EPL];
+
+  __device__ explicit DecodeWave(int lane) : row(lane / LPT), col(lane % LPT) {}
+
+  // query vectors of heads head0 .. head0 + G - 1 (zero for padded heads)
+  __device__ void load_q(const void* q, size_t head0, int G) {
+    const uint4* qs = reinterpret_cast<const uint4*>(q);
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+      qv[h] = (h < G) ? qs[((head0 + h) * D) / EPL + col] : make_uint4(0, 0, 0, 0);
+  }
+
+  __device__ void reset() {
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      m[h] = kNegInf;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+    }
+  }
+
+  // Blocks j = j_begin, j_begin + step, ... < j_end of the sequence whose table
+  // is tbl and whose visible length is L (j_end <= ceil(L / B)).
+  //
+  // A ring of NBUF register buffers: while block j is computed, the loads of
+  // the next NBUF-1 blocks are in flight, and the block id needed by the next
+  // issue is fetched one step ahead.  The ring is rotated by a fully unrolled
+  // loop, so every buffer index is a compile-time constant.  Loads are raw
+  // buffer loads with the (block, KV head) slice base built in SGPRs and no
+  // load under a branch, so each wait covers exactly the buffer consumed.  A
+  // block past the range gets a zero-size descriptor (zeros, no memory access).
+  //
+  // In the last block of a sequence the slots at or beyond L may hold anything
+  // (stale or poisoned data): every lane's slot is clamped to the last valid
+  // one, so only real tokens are loaded, and the scores of the clamped
+  // duplicates are set to -inf, which gives them weight exactly 0.
+  __device__ void run(const int32_t* tbl_ptr, int L, int j_begin, int j_end, int step,
+                      const char* kbase, const char* vbase, size_t blk_bytes, float scale_log2) {
+    const ConstI32Ptr tbl = as_const(tbl_ptr);
+    uint4 kbuf[NBUF][LPB], vbuf[NBUF][LPB];
+    auto load_block = [&](int jj, int phys, bool in_range, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
+      const int last = min(B - 1, L - 1 - jj * B);   // last valid slot (wave-uniform)
+      const int nrec = in_range ? kSliceBytes : 0;
+      const size_t boff = (size_t)phys * blk_bytes;
+      const BufRsrc rk = make_rsrc(kbase + boff, nrec);
+      const BufRsrc rv = make_rsrc(vbase + boff, nrec);
+      int voff[LPB];
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) voff[i] = min(i * TPL + row, last) * kRowBytes + col * 16;
+      // keep the issue order K then V, and both ahead of the compute that
+      // follows, so each wait covers exactly the buffer being consumed
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) kr[i] = buffer_load16(rk, voff[i]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) vr[i] = buffer_load16(rv, voff[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto compute_block = [&](int jj, const uint4 (&kr)[LPB], const uint4 (&vr)[LPB]) {
+      // QK: partial dot on the lane's 16 bytes, all-reduce over the token's lanes
+      float sc[LPB][GP];
+#pragma unroll
+      for (int i = 0; i < LPB; ++i)
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+          sc[i][h] = group_sum<LPT>(E::dot(qv[h], kr[i], 0.f)) * scale_log2;
+      if ((jj + 1) * B > L) {   // wave-uniform: only the last block of the sequence
+#pragma unroll
+        for (int i = 0; i < LPB; ++i) {
+          const bool valid = jj * B + i * TPL + row < L;
+#pragma unroll
+          for (int h = 0; h < GP; ++h) sc[i][h] = valid ? sc[i][h] : kNegInf;
+        }
+      }
+      // online softmax in base 2
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        float mx = m[h];
+#pragma unroll
+        for (int i = 0; i < LPB; ++i) mx = fmaxf(mx, sc[i][h]);
+        const float ms = (mx == kNegInf) ? 0.f : mx;
+        const float alpha = fast_exp2(m[h] - ms);
+        m[h] = mx;
+        sc[0][h] = fast_exp2(sc[0][h] - ms);
+        float psum = sc[0][h];
+#pragma unroll
+        for (int i = 1; i < LPB; ++i) {
+          sc[i][h] = fast_exp2(sc[i][h] - ms);
+          psum += sc[i][h];
+        }
+        l[h] = __builtin_fmaf(l[h], alpha, psum);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+      }
+      // PV: each V element is widened once and used for all GP heads
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) {
+        float vf[EPL];
+        E::to_float(vr[i], vf);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+#pragma unroll
+          for (int h = 0; h < GP; ++h) o[h][e] = __builtin_fmaf(sc[i][h], vf[e], o[h][e]);
+      }
+    };
+
+    if (j_begin >= j_end) return;
+    int j = j_begin;
+    const int jmax = j_end - 1;   // table reads are clamped here (always in bounds)
+#pragma unroll
+    for (int b = 0; b + 1 < NBUF; ++b) {
+      const int jb = j + b * step;
+      load_block(jb, tbl[min(jb, jmax)], jb < j_end, kbuf[b], vbuf[b]);
+    }
+    const int ahead = (NBUF - 1) * step;   // distance of the block issued next
+    int id_next = tbl[min(j + ahead, jmax)];
+    bool done = false;
+    while (!done) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        const int jn = j + ahead;
+        const int id_after = tbl[min(jn + step, jmax)];
+        load_block(jn, id_next, jn < j_end, kbuf[(u + NBUF - 1) % NBUF],
+                   vbuf[(u + NBUF - 1) % NBUF]);
+        compute_block(j, kbuf[u], vbuf[u]);
+        id_next = id_after;
+        j += step;
+        if (j >= j_end) {
+          done = true;
+          break;
+        }
+      }
+    }
+  }
+
+  // Merge the TPL token rows of the wave (lanes col, col + LPT, ...) by
+  // log-sum-exp; afterwards every row holds the wave's state.
+  __device__ void merge_rows_in_wave() {
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        const float m2 = __shfl_xor(m[h], off, 64);
+        const float l2 = __shfl_xor(l[h], off, 64);
+        const float mx = fmaxf(m[h], m2);
+        const float ms = (mx == kNegInf) ? 0.f : mx;
+        const float a1 = fast_exp2(m[h] - ms), a2 = fast_exp2(m2 - ms);
+        l[h] = l[h] * a1 + l2 * a2;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] = o[h][e] * a1 + __shfl_xor(o[h][e], off, 64) * a2;
+        m[h] = mx;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// split kernel: equal chunks of the flattened (sequence, KV head, block) list
+// ---------------------------------------------------------------------------
+// Items are numbered f = Hk pre[s] + g nb[s] + j (nb[s] = blocks of sequence
+// s, pre its exclusive prefix sum); wave w takes f in [w chunk, (w+1) chunk).
+// Workgroup 0 stores the plan for the merge: plan[0] = chunk, plan[1] = total
+// items, plan[2 ..] = pre[0 .. S].
+template <int DT, int D, int B, int GP>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a) {
+  using W = DecodeWave<DT, D, B, GP>;
+  extern __shared__ int sm_pre[];   // [S + 1] prefix sums of blocks per sequence
+  __shared__ int sm_scan[kThreads];
+  const int S = a.num_seqs, H = a.num_heads, Hk = a.num_kv_heads, G = a.group;
+  const int tid = threadIdx.x;
+
+  // block counts per sequence and their prefix sums (Hillis-Steele per 256)
+  int carry = 0;
+  if (tid == 0) sm_pre[0] = 0;
+  for (int base = 0; base < S; base += kThreads) {
+    const int s = base + tid;
+    const int L = s < S ? min(max(a.context_lens[s], 0), a.max_context_len) : 0;
+    int v = (L + B - 1) / B;
+    sm_scan[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int add = tid >= off ? sm_scan[tid - off] : 0;
+      __syncthreads();
+      v += add;
+      sm_scan[tid] = v;
+      __syncthreads();
+    }
+    if (s < S) sm_pre[s + 1] = carry + v;
+    carry += sm_scan[kThreads - 1];
+    __syncthreads();
+  }
+  const int total = Hk * __builtin_amdgcn_readfirstlane(sm_pre[S]);
+  const int nwaves = gridDim.x * kWaves;
+  const int chunk = a.chunk_blocks > 0 ? a.chunk_blocks : max(1, (total + nwaves - 1) / nwaves);
+  if (blockIdx.x == 0) {
+    if (tid == 0) {
+      a.plan[0] = chunk;
+      a.plan[1] = total;
+    }
+    for (int s = tid; s <= S; s += kThreads) a.plan[2 + s] = sm_pre[s];
+  }
+
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wid = blockIdx.x * kWaves + wave;
+  int f = wid * chunk;
+  const int f_end = min(f + chunk, total);
+  if (f >= total) return;
+
+  // Locate the first item: the sequence s with Hk pre[s] <= f < Hk pre[s+1].
+  // Values read from LDS are per-lane to the compiler; readfirstlane keeps the
+  // walk in scalar registers, so block ids come from scalar loads and the
+  // vector-memory waits in the block loop stay exact.
+  auto pre_at = [&](int i) { return __builtin_amdgcn_readfirstlane(sm_pre[i]); };
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (Hk * pre_at(mid) <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  int s = lo;
+  int nb = pre_at(s + 1) - pre_at(s);
+  const int r0 = f - Hk * pre_at(s);
+  int g = r0 / nb, j = r0 % nb;
+
+  W w(lane);
+  const size_t blk_bytes = (size_t)Hk * W::kSliceBytes;
+  const ConstI32Ptr lens = as_const(a.context_lens);
+  while (f < f_end) {
+    const int L = min(max(lens[s], 0), a.max_context_len);
+    const int n_here = min(nb - j, f_end - f);
+    const size_t head0 = (size_t)s * H + (size_t)g * G;
+    // drain the previous segment's stores (they share the vector-memory
+    // counter with loads) so the pipeline below starts from a known state
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    w.load_q(a.q, head0, G);
+    w.reset();
+    w.run(a.block_tables + (size_t)s * a.max_blocks_per_seq, L, j, j + n_here, 1,
+          static_cast<const char*>(a.k_cache) + (size_t)g * W::kSliceBytes,
+          static_cast<const char*>(a.v_cache) + (size_t)g * W::kSliceBytes, blk_bytes,
+          a.scale_log2);
+    w.merge_rows_in_wave();
+    if (w.row == 0) {
+      // (compile-time head loops keep the state in registers)
+      if (j == 0 && n_here == nb) {   // the whole (sequence, KV head): final output
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+          if (h >= G) break;
+          const float inv = w.l[h] > 0.f ? 1.f / w.l[h] : 0.f;
+#pragma unroll
+          for (int e = 0; e < W::EPL; ++e)
+            store_out(a.out, (head0 + h) * D + w.col * W::EPL + e, w.o[h][e] * inv, a.out_dtype);
+        }
+      } else {                        // a piece: partial for the merge
+        const size_t slot = ((size_t)s * Hk + g + wid) * G;
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+          if (h >= G) break;
+          float* po = a.ws_o + (slot + h) * D + w.col * W::EPL;
+#pragma unroll
+          for (int e = 0; e < W::EPL; ++e) po[e] = w.o[h][e];
+          if (w.col == 0) {
+            a.ws_ml[2 * (slot + h)] = w.m[h];
+            a.ws_ml[2 * (slot + h) + 1] = w.l[h];
+          }
+        }
+      }
+    }
+    f += n_here;
+    j += n_here;
+    if (j == nb && f < f_end) {       // next KV head, or the next non-empty sequence
+      j = 0;
+      if (++g == Hk) {
+        g = 0;
+        do {
+          ++s;
+        } while (pre_at(s + 1) == pre_at(s));
+        nb = pre_at(s + 1) - pre_at(s);
+      }
+    }
+  }
+}
+
+// Merge of one (sequence, KV head) of the split kernel: the waves whose chunks
+// cover its items [a0, a0 + nb) are a0 / chunk .. (a0 + nb - 1) / chunk, and
+// wave w left its piece in slot (s Hk + g + w).  Empty contexts get zero rows.
+template <int D>
+__global__ __launch_bounds__(kThreads) void split_merge_kernel(const AttnArgs a) {
+  const int g = blockIdx.x, s = blockIdx.y;
+  const int H = a.num_heads, Hk = a.num_kv_heads, G = a.group;
+  const int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  const size_t head0 = (size_t)s * H + (size_t)g * G;
+  if (L == 0) {
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+      store_out(a.out, head0 * D + i, 0.f, a.out_dtype);
+    return;
+  }
+  const int chunk = a.plan[0];
+  const int* pre = a.plan + 2;
+  const int nb = pre[s + 1] - pre[s];
+  const int a0 = Hk * pre[s] + g * nb;
+  const int w0 = a0 / chunk, w1 = (a0 + nb - 1) / chunk;
+  if (w0 == w1) return;               // written by its one wave
+  const size_t base = (size_t)s * Hk + g;
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int h = i / D, d = i % D;
+    float mx = kNegInf;
+    for (int w = w0; w <= w1; ++w) mx = fmaxf(mx, a.ws_ml[2 * ((base + w) * G + h)]);
+    const float ms = (mx == kNegInf) ? 0.f : mx;
+    float num = 0.f, den = 0.f;
+#pragma unroll 4
+    for (int w = w0; w <= w1; ++w) {
+      const size_t sl = (base + w) * G + h;
+      const float wt = fast_exp2(a.ws_ml[2 * sl] - ms);
+      num = __builtin_fmaf(wt, a.ws_o[sl * D + d], num);
+      den = __builtin_fmaf(wt, a.ws_ml[2 * sl + 1], den);
+    }
+    store_out(a.out, (head0 + h) * D + d, den > 0.f ? num / den : 0.f, a.out_dtype);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// partition kernel: one workgroup per (partition, KV head, row)
+// ---------------------------------------------------------------------------
+template <int DT, int D, int B, int GP>
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(const AttnArgs a) {
+  using W = DecodeWave<DT, D, B, GP>;
+  constexpr int EPL = W::EPL;
   const int p = blockIdx.x, g = blockIdx.y;
   const int H = a.num_heads, G = a.group;
   // Decode: blockIdx.z is the sequence and its one query row.  Per-row mode
   // (multi-token queries without MFMA): blockIdx.z = s * max_q_len + i is row i
   // of sequence s, which sees the first L_s - n_s + i + 1 keys when causal.
-  int s = blockIdx.z, qrow = blockIdx.z;
-  int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  int s = blockIdx.z, qrow = blockIdx.z, i = 0, n = 1;
   if (a.q_offsets) {
     s = blockIdx.z / a.max_q_len;
-    const int i = blockIdx.z % a.max_q_len;
-    const int q0 = a.q_offsets[s], n = a.q_offsets[s + 1] - q0;
+    i = blockIdx.z % a.max_q_len;
+    const int q0 = a.q_offsets[s];
+    n = a.q_offsets[s + 1] - q0;
     if (i >= n) return;
     qrow = q0 + i;
-    L = min(max(a.context_lens[s], 0), a.max_context_len);
-    if (a.causal) L = max(0, min(L, L - n + i + 1));
   }
+  // context_lens is read only once s is known (blockIdx.z may exceed S)
+  int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  if (a.q_offsets && a.causal) L = max(0, min(L, L - n + i + 1));
   const int n_parts = (L + a.part - 1) / a.part;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
-  const int row = lane / LPT, col = lane % LPT;
-  const size_t head0 = (size_t)qrow * H + (size_t)g * G;   // first query head of the group
+  const size_t head0 = (size_t)qrow * H + (size_t)g * G;       // first query head of the group
 
   if (n_parts == 0) {  // empty context: zero output rows, written by partition 0
     if (p == 0)
@@ -77,183 +417,28 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const AttnArgs
   }
   if (p >= n_parts) return;
 
-  // query vectors of the group (zero for padded heads h >= G)
-  uint4 qv[GP];
-  const uint4* qsrc = reinterpret_cast<const uint4*>(a.q);
-#pragma unroll
-  for (int h = 0; h < GP; ++h) {
-    if (h < G) qv[h] = qsrc[((head0 + h) * D) / EPL + col];
-    else qv[h] = make_uint4(0, 0, 0, 0);
-  }
-
-  float m[GP], l[GP], o[GP][EPL];
-#pragma unroll
-  for (int h = 0; h < GP; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
-  }
-
+  W w(lane);
+  w.load_q(a.q, head0, G);
+  w.reset();
   const int tok0 = p * a.part;
-  const int tok_end = min(tok0 + a.part, L);
-  const int blk_end = (tok_end + B - 1) / B;
-  const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
-  const uint4* kc = reinterpret_cast<const uint4*>(a.k_cache);
-  const uint4* vc = reinterpret_cast<const uint4*>(a.v_cache);
-  // vector index of (block phys, head g, row 0, col) and the stride between
-  // the TPL-token groups of a block
-  constexpr int kVecPerBlockHead = B * D / EPL;
-  const size_t lane_off = (size_t)row * (D / EPL) + col;
-  const size_t head_off = (size_t)g * kVecPerBlockHead;
-  const size_t blk_stride = (size_t)a.num_kv_heads * kVecPerBlockHead;
-
-  // A ring of NBUF register buffers per wave: while block j is computed, the
-  // loads of blocks j + kWaves .. j + (NBUF-1) kWaves are in flight, and the
-  // block id needed by the next issue is fetched one step ahead.  The ring is
-  // rotated by a fully unrolled loop, so every buffer index is a compile-time
-  // constant (registers, never scratch).
-  //
-  // Loads are raw buffer loads: the (block, KV head) slice base is built in
-  // SGPRs from the block id, each lane adds a fixed offset, and no load sits
-  // under a branch, so the compiler can wait for exactly the buffer it needs.
-  // A block past the wave's range gets a zero-size descriptor: its loads
-  // return zeros without touching memory.
-  //
-  // In the last block of a sequence the slots at or beyond L may hold anything
-  // (stale or poisoned data).  There every lane's slot is clamped to the last
-  // valid one, so only real tokens are ever loaded, and the scores of the
-  // clamped duplicates are set to -inf: they get weight exactly 0.
-  constexpr int kRowBytes = D * E::kBytes;
-  constexpr int kSliceBytes = B * kRowBytes;   // one (block, KV head) slice
-  const size_t blk_bytes = (size_t)a.num_kv_heads * kSliceBytes;
-  const char* kbase = static_cast<const char*>(a.k_cache) + (size_t)g * kSliceBytes;
-  const char* vbase = static_cast<const char*>(a.v_cache) + (size_t)g * kSliceBytes;
-  uint4 kbuf[NBUF][LPB], vbuf[NBUF][LPB];
-  auto load_block = [&](int jj, int phys, bool in_range, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
-    const int last = min(B - 1, L - 1 - jj * B);   // last valid slot (wave-uniform)
-    const int nrec = in_range ? kSliceBytes : 0;
-    const size_t boff = (size_t)phys * blk_bytes;
-    const BufRsrc rk = make_rsrc(kbase + boff, nrec);
-    const BufRsrc rv = make_rsrc(vbase + boff, nrec);
-    int voff[LPB];
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) voff[i] = min(i * TPL + row, last) * kRowBytes + col * 16;
-    // keep the issue order K then V, and keep both ahead of the compute that
-    // follows, so each wait covers exactly the buffer being consumed
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) kr[i] = buffer_load16(rk, voff[i]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) vr[i] = buffer_load16(rv, voff[i]);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  auto compute_block = [&](int jj, const uint4 (&kr)[LPB], const uint4 (&vr)[LPB]) {
-    // QK: partial dot on the lane's 16 bytes, all-reduce over the token's lanes
-    float sc[LPB][GP];
-#pragma unroll
-    for (int i = 0; i < LPB; ++i)
-#pragma unroll
-      for (int h = 0; h < GP; ++h)
-        sc[i][h] = group_sum<LPT>(E::dot(qv[h], kr[i], 0.f)) * a.scale_log2;
-    if ((jj + 1) * B > L) {   // wave-uniform: only the last block of the sequence
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        const bool valid = jj * B + i * TPL + row < L;
-#pragma unroll
-        for (int h = 0; h < GP; ++h) sc[i][h] = valid ? sc[i][h] : kNegInf;
-      }
-    }
-    // online softmax in base 2
-#pragma unroll
-    for (int h = 0; h < GP; ++h) {
-      float mx = m[h];
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) mx = fmaxf(mx, sc[i][h]);
-      const float ms = (mx == kNegInf) ? 0.f : mx;
-      const float alpha = fast_exp2(m[h] - ms);
-      m[h] = mx;
-      sc[0][h] = fast_exp2(sc[0][h] - ms);
-      float psum = sc[0][h];
-#pragma unroll
-      for (int i = 1; i < LPB; ++i) {
-        sc[i][h] = fast_exp2(sc[i][h] - ms);
-        psum += sc[i][h];
-      }
-      l[h] = __builtin_fmaf(l[h], alpha, psum);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
-    }
-    // PV: each V element is widened once and used for all GP heads
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) {
-      float vf[EPL];
-      E::to_float(vr[i], vf);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e)
-#pragma unroll
-        for (int h = 0; h < GP; ++h) o[h][e] = __builtin_fmaf(sc[i][h], vf[e], o[h][e]);
-    }
-  };
-
-  // blocks of this wave: j, j + kWaves, j + 2 kWaves, ... < blk_end
-  int j = tok0 / B + wave;
-  const int jmax = blk_end - 1;   // table reads are clamped here (always in bounds)
-#pragma unroll
-  for (int b = 0; b + 1 < NBUF; ++b) {
-    const int jb = j + b * kWaves;
-    load_block(jb, tbl[min(jb, jmax)], jb < blk_end, kbuf[b], vbuf[b]);
-  }
-  constexpr int kAhead = (NBUF - 1) * kWaves;   // distance of the block issued next
-  int id_next = tbl[min(j + kAhead, jmax)];
-  bool done = j >= blk_end;
-  while (!done) {
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      const int jn = j + kAhead;
-      const int id_after = tbl[min(jn + kWaves, jmax)];
-      load_block(jn, id_next, jn < blk_end, kbuf[(u + NBUF - 1) % NBUF],
-                 vbuf[(u + NBUF - 1) % NBUF]);
-      compute_block(j, kbuf[u], vbuf[u]);
-      id_next = id_after;
-      j += kWaves;
-      if (j >= blk_end) {
-        done = true;
-        break;
-      }
-    }
-  }
-
-  // merge the TPL token rows of the wave (lanes col, col+LPT, ...)
-#pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < GP; ++h) {
-      const float m2 = __shfl_xor(m[h], off, 64);
-      const float l2 = __shfl_xor(l[h], off, 64);
-      const float mx = fmaxf(m[h], m2);
-      const float ms = (mx == kNegInf) ? 0.f : mx;
-      const float a1 = fast_exp2(m[h] - ms), a2 = fast_exp2(m2 - ms);
-      l[h] = l[h] * a1 + l2 * a2;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[h][e] = o[h][e] * a1 + __shfl_xor(o[h][e], off, 64) * a2;
-      m[h] = mx;
-    }
-  }
+  const int blk_end = (min(tok0 + a.part, L) + B - 1) / B;
+  w.run(a.block_tables + (size_t)s * a.max_blocks_per_seq, L, tok0 / B + wave, blk_end, kWaves,
+        static_cast<const char*>(a.k_cache) + (size_t)g * W::kSliceBytes,
+        static_cast<const char*>(a.v_cache) + (size_t)g * W::kSliceBytes,
+        (size_t)a.num_kv_heads * W::kSliceBytes, a.scale_log2);
+  w.merge_rows_in_wave();
 
   // merge the waves through LDS
   __shared__ float sm_o[kWaves][GP][D];
   __shared__ float sm_m[kWaves][GP], sm_l[kWaves][GP];
-  if (row == 0) {
+  if (w.row == 0) {
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_o[wave][h][col * EPL + e] = o[h][e];
-      if (col == 0) {
-        sm_m[wave][h] = m[h];
-        sm_l[wave][h] = l[h];
+      for (int e = 0; e < EPL; ++e) sm_o[wave][h][w.col * EPL + e] = w.o[h][e];
+      if (w.col == 0) {
+        sm_m[wave][h] = w.m[h];
+        sm_l[wave][h] = w.l[h];
       }
     }
   }
@@ -264,14 +449,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const AttnArgs
     const int h = i / D, d = i % D;
     float mx = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    for (int v = 0; v < kWaves; ++v) mx = fmaxf(mx, sm_m[v][h]);
     const float ms = (mx == kNegInf) ? 0.f : mx;
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float wt = fast_exp2(sm_m[w][h] - ms);
-      num = __builtin_fmaf(wt, sm_o[w][h][d], num);
-      den = __builtin_fmaf(wt, sm_l[w][h], den);
+    for (int v = 0; v < kWaves; ++v) {
+      const float wt = fast_exp2(sm_m[v][h] - ms);
+      num = __builtin_fmaf(wt, sm_o[v][h][d], num);
+      den = __builtin_fmaf(wt, sm_l[v][h], den);
     }
     const size_t hh = head0 + h;
     if (final_out) {
@@ -314,8 +499,8 @@ __device__ inline void merge_rows(const AttnArgs& a, size_t row, int g, int n_pa
   }
 }
 
-// Separate merge launch.  Rows with a single partition were finished by the
-// partial kernel.
+// Merge of the partition kernel's (and the multi-query kernel's) partials.
+// Rows with a single partition were finished by the partition kernel.
 template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const AttnArgs a) {
   const int g = blockIdx.y, s = blockIdx.z;
@@ -334,9 +519,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dispatch
+// launch
 // ---------------------------------------------------------------------------
-// Merge launch shared with the multi-query kernel (rows = query tokens).
 hipError_t launch_merge(int head_dim, int num_seqs, const AttnArgs& a, hipStream_t st) {
   dim3 mgrid(a.q_offsets ? a.max_q_len : 1, a.num_kv_heads, num_seqs);
   if (head_dim == 64)
@@ -346,54 +530,86 @@ hipError_t launch_merge(int head_dim, int num_seqs, const AttnArgs& a, hipStream
   return hipGetLastError();
 }
 
+// Resident workgroups per CU of the split kernel (occupancy query, cached).
+template <int DT, int D, int B, int GP>
+static int split_wgs_per_cu() {
+  static int cached = 0;
+  if (!cached) {
+    int n = 0;
+    const size_t smem = ((size_t)kMaxSplitSeqs + 1) * sizeof(int);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(decode_split_kernel<DT, D, B, GP>), kThreads,
+            smem) != hipSuccess || n < 1)
+      n = 1;
+    cached = n;
+  }
+  return cached;
+}
+
 template <int DT, int D, int B, int GP>
 static hipError_t launch_decode_t(int num_seqs, const AttnArgs& a, hipStream_t st,
                                   const KernelEvents& ev) {
+  if (a.plan) {   // balanced split
+    const size_t smem = ((size_t)num_seqs + 1) * sizeof(int);
+    if (ev.start) (void)hipEventRecord(ev.start, st);
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, B, GP>), dim3(a.split_workgroups),
+                       dim3(kThreads), smem, st, a);
+    hipError_t e = hipGetLastError();
+    if (ev.stop) (void)hipEventRecord(ev.stop, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((split_merge_kernel<D>), dim3(a.num_kv_heads, num_seqs), dim3(kThreads),
+                       0, st, a);
+    return hipGetLastError();
+  }
   // per-row mode launches one grid row per (sequence, query row) slot
   const int rows = a.q_offsets ? num_seqs * a.max_q_len : num_seqs;
   dim3 grid(a.max_parts, a.num_kv_heads, rows);
-  if (ev.start) hipEventRecord(ev.start, st);
-  hipLaunchKernelGGL((decode_partial_kernel<DT, D, B, GP>), grid, dim3(kThreads), 0, st, a);
+  if (ev.start) (void)hipEventRecord(ev.start, st);
+  hipLaunchKernelGGL((decode_partition_kernel<DT, D, B, GP>), grid, dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (ev.stop) hipEventRecord(ev.stop, st);
+  if (ev.stop) (void)hipEventRecord(ev.stop, st);
   if (e != hipSuccess || a.max_parts <= 1) return e;
   return launch_merge(D, num_seqs, a, st);
 }
 
-template <int DT, int D, int B>
-static hipError_t dispatch_g(int group, int num_seqs, const AttnArgs& a, hipStream_t st,
-                             const KernelEvents& ev) {
-  if (group <= 1) return launch_decode_t<DT, D, B, 1>(num_seqs, a, st, ev);
-  if (group <= 2) return launch_decode_t<DT, D, B, 2>(num_seqs, a, st, ev);
-  if (group <= 4) return launch_decode_t<DT, D, B, 4>(num_seqs, a, st, ev);
-  if (group <= 8) return launch_decode_t<DT, D, B, 8>(num_seqs, a, st, ev);
-  return launch_decode_t<DT, D, B, 16>(num_seqs, a, st, ev);
-}
-
-template <int DT, int D>
-static hipError_t dispatch_b(int block_size, int group, int num_seqs, const AttnArgs& a,
-                             hipStream_t st, const KernelEvents& ev) {
-  switch (block_size) {
-    case 8: return dispatch_g<DT, D, 8>(group, num_seqs, a, st, ev);
-    case 16: return dispatch_g<DT, D, 16>(group, num_seqs, a, st, ev);
-    default: return dispatch_g<DT, D, 32>(group, num_seqs, a, st, ev);
-  }
-}
-
-template <int DT>
-static hipError_t dispatch_d(int head_dim, int block_size, int group, int num_seqs,
-                             const AttnArgs& a, hipStream_t st, const KernelEvents& ev) {
-  if (head_dim == 64) return dispatch_b<DT, 64>(block_size, group, num_seqs, a, st, ev);
-  return dispatch_b<DT, 128>(block_size, group, num_seqs, a, st, ev);
+// Compile-time dispatch over (dtype, head_dim, block_size, padded group).
+template <typename F>
+static auto with_config(int dtype, int head_dim, int block_size, int group, F&& f) {
+  auto by_g = [&](auto dt, auto d, auto b) {
+    using I1 = std::integral_constant<int, 1>;
+    if (group <= 1) return f(dt, d, b, I1{});
+    if (group <= 2) return f(dt, d, b, std::integral_constant<int, 2>{});
+    if (group <= 4) return f(dt, d, b, std::integral_constant<int, 4>{});
+    if (group <= 8) return f(dt, d, b, std::integral_constant<int, 8>{});
+    return f(dt, d, b, std::integral_constant<int, 16>{});
+  };
+  auto by_b = [&](auto dt, auto d) {
+    if (block_size == 8) return by_g(dt, d, std::integral_constant<int, 8>{});
+    if (block_size == 16) return by_g(dt, d, std::integral_constant<int, 16>{});
+    return by_g(dt, d, std::integral_constant<int, 32>{});
+  };
+  auto by_d = [&](auto dt) {
+    if (head_dim == 64) return by_b(dt, std::integral_constant<int, 64>{});
+    return by_b(dt, std::integral_constant<int, 128>{});
+  };
+  if (dtype == PA_F32) return by_d(std::integral_constant<int, PA_F32>{});
+  if (dtype == PA_F16) return by_d(std::integral_constant<int, PA_F16>{});
+  return by_d(std::integral_constant<int, PA_BF16>{});
 }
 
 hipError_t launch_decode(int dtype, int head_dim, int block_size, int group, int num_seqs,
                          const AttnArgs& a, hipStream_t st, const KernelEvents& ev) {
-  switch (dtype) {
-    case PA_F32: return dispatch_d<PA_F32>(head_dim, block_size, group, num_seqs, a, st, ev);
-    case PA_F16: return dispatch_d<PA_F16>(head_dim, block_size, group, num_seqs, a, st, ev);
-    default: return dispatch_d<PA_BF16>(head_dim, block_size, group, num_seqs, a, st, ev);
-  }
+  return with_config(dtype, head_dim, block_size, group, [&](auto dt, auto d, auto b, auto gp) {
+    return launch_decode_t<decltype(dt)::value, decltype(d)::value, decltype(b)::value,
+                           decltype(gp)::value>(num_seqs, a, st, ev);
+  });
+}
+
+int split_workgroups_per_cu(int dtype, int head_dim, int block_size, int group) {
+  return with_config(dtype, head_dim, block_size, group, [&](auto dt, auto d, auto b, auto gp) {
+    return split_wgs_per_cu<decltype(dt)::value, decltype(d)::value, decltype(b)::value,
+                            decltype(gp)::value>();
+  });
 }
 
 }  // namespace pa

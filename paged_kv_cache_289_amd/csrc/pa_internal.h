@@ -18,6 +18,11 @@ namespace pa {
 constexpr int kWaves = PA_WAVES;
 constexpr int kThreads = 64 * kWaves;
 
+// Balanced-split decode: most sequences per call it handles (their prefix sums
+// live in LDS), and most waves it launches (the workspace is sized for this).
+constexpr int kMaxSplitSeqs = 8192;
+constexpr int kMaxSplitWaves = 8192;
+
 // Arguments of the decode / multi-query partial kernels and of the merge.
 struct AttnArgs {
   void* out;                 // [rows][H][D], out_dtype
@@ -29,6 +34,7 @@ struct AttnArgs {
   const int32_t* block_tables;  // [S][mbs]
   const int32_t* context_lens;  // [S]
   const int32_t* q_offsets;     // [S+1] (multi-query only)
+  int num_seqs;              // S
   int num_heads;             // H
   int num_kv_heads;          // Hk
   int group;                 // G = H / Hk
@@ -40,6 +46,10 @@ struct AttnArgs {
   int causal;
   int out_dtype;
   float scale_log2;          // scale * log2(e): scores are kept in log2 units
+  // balanced-split decode (plan != nullptr)
+  int* plan;                 // [2 + S + 1]: chunk, total items, block prefix sums
+  int chunk_blocks;          // items per wave (0: split evenly over the launch)
+  int split_workgroups;      // workgroups launched
 };
 
 // Optional events recorded right around a call's main kernel (profiling aid).
@@ -50,6 +60,9 @@ struct KernelEvents {
 
 hipError_t launch_decode(int dtype, int head_dim, int block_size, int group, int num_seqs,
                          const AttnArgs& a, hipStream_t stream, const KernelEvents& ev);
+
+// Resident workgroups per CU of the split decode kernel for this configuration.
+int split_workgroups_per_cu(int dtype, int head_dim, int block_size, int group);
 
 hipError_t launch_multiq(int dtype, int head_dim, int block_size, int group, int num_seqs,
                          const AttnArgs& a, hipStream_t stream, const KernelEvents& ev);

@@ -288,10 +288,10 @@ static hipError_t launch_mfma_t(int num_seqs, const AttnArgs& a, hipStream_t st,
                                 const KernelEvents& ev) {
   const int rt_count = (a.max_q_len * a.group + 31) / 32;
   dim3 grid(rt_count * a.max_parts, a.num_kv_heads, num_seqs);
-  if (ev.start) hipEventRecord(ev.start, st);
+  if (ev.start) (void)hipEventRecord(ev.start, st);
   hipLaunchKernelGGL((multiq_mfma_kernel<DT, D, B>), grid, dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (ev.stop) hipEventRecord(ev.stop, st);
+  if (ev.stop) (void)hipEventRecord(ev.stop, st);
   if (e != hipSuccess || a.max_parts <= 1) return e;
   return launch_merge(D, num_seqs, a, st);
 }

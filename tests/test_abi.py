@@ -109,11 +109,16 @@ def test_gather_and_check_reject_bad_arguments_on_host():
 
 
 def test_workspace_size_formula():
-    # 64 sequences x 32 heads, head_dim 128, contexts up to 4096 in 256-token partitions:
-    # 16 partitions x (128 outputs + max + sum) fp32 per (sequence, head)
+    # Decode, 64 sequences x 8 KV heads (G = 4), head_dim 128, contexts up to 4096 in
+    # 16-token blocks, 256-token pieces: at most 64*8*256 = 131072 items in pieces of 16
+    # blocks -> 8192 waves; the plan (2 + 65 ints, 16-byte rounded) then fp32 (max, sum)
+    # and outputs for (64*8 + 8192) slots x 4 heads.
     n = ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 256)
-    assert n == 64 * 32 * 16 * 130 * 4
-    assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 256, 256) == 0     # one partition
+    assert n == 272 + (64 * 8 + 8192) * 4 * 130 * 4
+    # default pieces: the launch never exceeds 8192 waves
+    assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 0) == n
+    # multi-token rows whose contexts fit one partition need no workspace
+    assert ops.workspace_size(2, 10, 5, 32, 8, 128, 16, 256, 0) == 0
     assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 24) == 0     # rejected
     assert ops.default_partition(64, 32, 8, 16, 4096, 1) % 16 == 0
     assert ops.default_partition(1, 32, 8, 16, 4608, 512) % 32 == 0
