@@ -32,6 +32,13 @@ template <> struct Elem<PA_F32> {
     acc = __builtin_fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
     return acc;
   }
+  __device__ static inline float dot0(const uint4& q, const uint4& k) {
+    float acc = __uint_as_float(q.x) * __uint_as_float(k.x);
+    acc = __builtin_fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+    acc = __builtin_fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+    acc = __builtin_fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+    return acc;
+  }
   __device__ static inline void to_float(const uint4& v, float* f) {
     f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
@@ -55,6 +62,16 @@ template <> struct Elem<PA_BF16> {
     acc = dot2(q.w, k.w, acc);
     return acc;
   }
+  // dot(q, k, 0) with the first step in the three-operand form, which takes the
+  // zero as an inline constant instead of a zeroed accumulator register
+  __device__ static inline float dot0(const uint4& q, const uint4& k) {
+    float acc;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(q.x), "v"(k.x));
+    acc = dot2(q.y, k.y, acc);
+    acc = dot2(q.z, k.z, acc);
+    acc = dot2(q.w, k.w, acc);
+    return acc;
+  }
   __device__ static inline void to_float(const uint4& v, float* f) {
     f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
     f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
@@ -70,6 +87,14 @@ template <> struct Elem<PA_F16> {
   }
   __device__ static inline float dot(const uint4& q, const uint4& k, float acc) {
     acc = dot2(q.x, k.x, acc);
+    acc = dot2(q.y, k.y, acc);
+    acc = dot2(q.z, k.z, acc);
+    acc = dot2(q.w, k.w, acc);
+    return acc;
+  }
+  __device__ static inline float dot0(const uint4& q, const uint4& k) {
+    float acc;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(acc) : "v"(q.x), "v"(k.x));
     acc = dot2(q.y, k.y, acc);
     acc = dot2(q.z, k.z, acc);
     acc = dot2(q.w, k.w, acc);
@@ -131,6 +156,32 @@ __device__ inline float group_sum(float x) {
   if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
   if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
   return x;
+}
+
+// group_sum over a whole array: step by step across all entries, so every DPP
+// read is far from the write that produced its operand.
+template <int N, int K>
+__device__ inline void group_sum_all(float (&x)[K]) {
+  if constexpr (N >= 2) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) x[k] += dpp<kDppQuadXor1>(x[k]);
+  }
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) x[k] += dpp<kDppQuadXor2>(x[k]);
+  }
+  if constexpr (N >= 8) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) x[k] += dpp<kDppRowHalfMirror>(x[k]);
+  }
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) x[k] += dpp<kDppRowMirror>(x[k]);
+  }
+  if constexpr (N >= 32) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) x[k] += __shfl_xor(x[k], 16, 64);
+  }
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -14,8 +14,16 @@
 //
 // Per block: QK partial dots (bf16/f16 dot2, fp32 FMA for f32) on the lane's
 // 16 bytes, a DPP all-reduce over the LPT lanes of the token, online softmax in
-// base 2 (scores pre-multiplied by scale*log2 e), and PV accumulated in fp32 on
-// the same lanes, which already hold that token's V dims.
+// base 2 (the scale times log2 e is applied inside the exponent's FMA), and PV
+// accumulated in fp32 on the same lanes, which already hold that token's V dims.
+//
+// Lazy rescaling.  The running max m only moves when a score exceeds it by
+// more than kRescaleLog2 (log2 units); otherwise the block's weights are taken
+// against the stale m, so they are at most 2^kRescaleLog2 and the o / l
+// rescale is skipped.  After the first block of a run that is nearly every
+// block.  o and l always refer to the stored m, so partials and merges are
+// unchanged.  m starts at a finite sentinel, which keeps rows without any
+// valid token free of inf - inf.
 //
 // Two ways to cut the work into waves:
 //  * split (decode default): every (sequence, KV head, block) item is numbered
@@ -38,6 +46,14 @@ namespace pa {
 #define PA_NBUF 2
 #endif
 constexpr int NBUF = PA_NBUF;   // register ring depth: blocks in flight per wave + 1
+constexpr float kRescaleLog2 = 8.f;
+constexpr float kMaxInit = -1e30f;   // running-max sentinel (below any real score)
+
+// Positive exponent scale for scale_log2 (the sign goes into q, 0 into a tiny
+// value that leaves every weight at exactly 1).
+__device__ inline float exp_scale(float scale_log2) {
+  return fmaxf(fabsf(scale_log2), 1e-30f);
+}
 
 // ---------------------------------------------------------------------------
 // one wave's walk over some blocks of one (row, KV head)
@@ -59,18 +75,23 @@ struct DecodeWave {
 
   __device__ explicit DecodeWave(int lane) : row(lane / LPT), col(lane % LPT) {}
 
-  // query vectors of heads head0 .. head0 + G - 1 (zero for padded heads)
-  __device__ void load_q(const void* q, size_t head0, int G) {
+  // query vectors of heads head0 .. head0 + G - 1 (zero for padded heads),
+  // sign-flipped when the scale is negative (exact in every storage type)
+  __device__ void load_q(const void* q, size_t head0, int G, float scale_log2) {
     const uint4* qs = reinterpret_cast<const uint4*>(q);
+    const uint32_t flip = scale_log2 < 0.f ? (E::kBytes == 4 ? 0x80000000u : 0x80008000u) : 0u;
 #pragma unroll
-    for (int h = 0; h < GP; ++h)
-      qv[h] = (h < G) ? qs[((head0 + h) * D) / EPL + col] : make_uint4(0, 0, 0, 0);
+    for (int h = 0; h < GP; ++h) {
+      uint4 v = (h < G) ? qs[((head0 + h) * D) / EPL + col] : make_uint4(0, 0, 0, 0);
+      v.x ^= flip; v.y ^= flip; v.z ^= flip; v.w ^= flip;
+      qv[h] = v;
+    }
   }
 
   __device__ void reset() {
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
-      m[h] = kNegInf;
+      m[h] = kMaxInit;
       l[h] = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
@@ -95,6 +116,7 @@ struct DecodeWave {
   __device__ void run(const int32_t* tbl_ptr, int L, int j_begin, int j_end, int step,
                       const char* kbase, const char* vbase, size_t blk_bytes, float scale_log2) {
     const ConstI32Ptr tbl = as_const(tbl_ptr);
+    const float c = exp_scale(scale_log2);
     uint4 kbuf[NBUF][LPB], vbuf[NBUF][LPB];
     auto load_block = [&](int jj, int phys, bool in_range, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
       const int last = min(B - 1, L - 1 - jj * B);   // last valid slot (wave-uniform)
@@ -118,13 +140,19 @@ struct DecodeWave {
 
     auto compute_block = [&](int jj, const uint4 (&kr)[LPB], const uint4 (&vr)[LPB]) {
       // QK: partial dot on the lane's 16 bytes, all-reduce over the token's lanes
+      float part[LPB * GP];
+#pragma unroll
+      for (int i = 0; i < LPB; ++i)
+#pragma unroll
+        for (int h = 0; h < GP; ++h) part[i * GP + h] = E::dot0(qv[h], kr[i]);
+      group_sum_all<LPT>(part);
       float sc[LPB][GP];
 #pragma unroll
       for (int i = 0; i < LPB; ++i)
 #pragma unroll
-        for (int h = 0; h < GP; ++h)
-          sc[i][h] = group_sum<LPT>(E::dot(qv[h], kr[i], 0.f)) * scale_log2;
+        for (int h = 0; h < GP; ++h) sc[i][h] = part[i * GP + h];
       if ((jj + 1) * B > L) {   // wave-uniform: only the last block of the sequence
+        asm volatile("");       // keep this a branch (not selects on every block)
 #pragma unroll
         for (int i = 0; i < LPB; ++i) {
           const bool valid = jj * B + i * TPL + row < L;
@@ -132,25 +160,37 @@ struct DecodeWave {
           for (int h = 0; h < GP; ++h) sc[i][h] = valid ? sc[i][h] : kNegInf;
         }
       }
-      // online softmax in base 2
+      // online softmax in base 2 with lazy rescaling
+      float mb[GP];
+      bool up = false;
 #pragma unroll
       for (int h = 0; h < GP; ++h) {
-        float mx = m[h];
+        float t = sc[0][h];
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) mx = fmaxf(mx, sc[i][h]);
-        const float ms = (mx == kNegInf) ? 0.f : mx;
-        const float alpha = fast_exp2(m[h] - ms);
-        m[h] = mx;
-        sc[0][h] = fast_exp2(sc[0][h] - ms);
-        float psum = sc[0][h];
+        for (int i = 1; i < LPB; ++i) t = fmaxf(t, sc[i][h]);
+        mb[h] = t * c;
+        up |= mb[h] > m[h] + kRescaleLog2;
+      }
+      if (__builtin_amdgcn_ballot_w64(up) != 0) {   // wave-uniform, rare
 #pragma unroll
-        for (int i = 1; i < LPB; ++i) {
-          sc[i][h] = fast_exp2(sc[i][h] - ms);
+        for (int h = 0; h < GP; ++h) {
+          const float mn = fmaxf(m[h], mb[h]);
+          const float alpha = fast_exp2(m[h] - mn);
+          m[h] = mn;
+          l[h] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < LPB; ++i) {
+          sc[i][h] = fast_exp2(__builtin_fmaf(sc[i][h], c, -m[h]));
           psum += sc[i][h];
         }
-        l[h] = __builtin_fmaf(l[h], alpha, psum);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+        l[h] += psum;
       }
       // PV: each V element is widened once and used for all GP heads
 #pragma unroll
@@ -293,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
     // drain the previous segment's stores (they share the vector-memory
     // counter with loads) so the pipeline below starts from a known state
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    w.load_q(a.q, head0, G);
+    w.load_q(a.q, head0, G, a.scale_log2);
     w.reset();
     w.run(a.block_tables + (size_t)s * a.max_blocks_per_seq, L, j, j + n_here, 1,
           static_cast<const char*>(a.k_cache) + (size_t)g * W::kSliceBytes,
@@ -418,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const AttnAr
   if (p >= n_parts) return;
 
   W w(lane);
-  w.load_q(a.q, head0, G);
+  w.load_q(a.q, head0, G, a.scale_log2);
   w.reset();
   const int tok0 = p * a.part;
   const int blk_end = (min(tok0 + a.part, L) + B - 1) / B;
