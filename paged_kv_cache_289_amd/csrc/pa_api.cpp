@@ -225,6 +225,7 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
   a.num_kv_heads = num_kv_heads;
   a.group = num_heads / num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.pool_blocks = num_blocks;
   a.max_context_len = max_context_len;
   a.max_q_len = 1;
   a.causal = 0;
@@ -308,6 +309,7 @@ int paged_attn_multiq(void* out, const void* q, const void* k_cache, const void*
   a.num_kv_heads = num_kv_heads;
   a.group = num_heads / num_kv_heads;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.pool_blocks = num_blocks;
   a.max_context_len = max_context_len;
   a.part = part;
   a.max_parts = max_parts;

@@ -208,6 +208,8 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // Descriptor word 3 for untyped dword access on gfx9-family parts.
 constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of buffer loads: the nt bit.
+constexpr int kCpolNt = 2;
 
 // A descriptor covering nbytes from base; accesses at or past nbytes return
 // zero without touching memory.
@@ -218,6 +220,13 @@ __device__ inline BufRsrc make_rsrc(const void* base, int nbytes) {
 
 __device__ inline uint4 buffer_load16(BufRsrc r, int byte_off) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The same load with the non-temporal hint (nt): the line is read once, so the
+// caches should not keep it at the expense of data that is reused.
+__device__ inline uint4 buffer_load16_nt(BufRsrc r, int byte_off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCpolNt);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 

@@ -113,6 +113,11 @@ struct DecodeWave {
   // (stale or poisoned data): every lane's slot is clamped to the last valid
   // one, so only real tokens are loaded, and the scores of the clamped
   // duplicates are set to -inf, which gives them weight exactly 0.
+  //
+  // Streaming (NT) loads carry the non-temporal hint: K/V bytes that no other
+  // wave reads again should not push reused lines (block tables, queries,
+  // partials, and shared blocks) out of the caches.
+  template <bool NT>
   __device__ void run(const int32_t* tbl_ptr, int L, int j_begin, int j_end, int step,
                       const char* kbase, const char* vbase, size_t blk_bytes, float scale_log2) {
     const ConstI32Ptr tbl = as_const(tbl_ptr);
@@ -131,10 +136,10 @@ struct DecodeWave {
       // follows, so each wait covers exactly the buffer being consumed
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) kr[i] = buffer_load16(rk, voff[i]);
+      for (int i = 0; i < LPB; ++i) kr[i] = NT ? buffer_load16_nt(rk, voff[i]) : buffer_load16(rk, voff[i]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) vr[i] = buffer_load16(rv, voff[i]);
+      for (int i = 0; i < LPB; ++i) vr[i] = NT ? buffer_load16_nt(rv, voff[i]) : buffer_load16(rv, voff[i]);
       __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -290,6 +295,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
     __syncthreads();
   }
   const int total = Hk * __builtin_amdgcn_readfirstlane(sm_pre[S]);
+  // More table entries than pool blocks means some block serves several
+  // sequences (a shared prefix): then K/V lines are worth keeping in the
+  // caches.  Otherwise every block is (almost surely) read once: stream it.
+  const bool stream = total / Hk <= a.pool_blocks;
   const int nwaves = gridDim.x * kWaves;
   const int chunk = a.chunk_blocks > 0 ? a.chunk_blocks : max(1, (total + nwaves - 1) / nwaves);
   if (blockIdx.x == 0) {
@@ -335,10 +344,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     w.load_q(a.q, head0, G, a.scale_log2);
     w.reset();
-    w.run(a.block_tables + (size_t)s * a.max_blocks_per_seq, L, j, j + n_here, 1,
-          static_cast<const char*>(a.k_cache) + (size_t)g * W::kSliceBytes,
-          static_cast<const char*>(a.v_cache) + (size_t)g * W::kSliceBytes, blk_bytes,
-          a.scale_log2);
+    const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+    const char* kb = static_cast<const char*>(a.k_cache) + (size_t)g * W::kSliceBytes;
+    const char* vb = static_cast<const char*>(a.v_cache) + (size_t)g * W::kSliceBytes;
+    if (stream)
+      w.template run<true>(tbl, L, j, j + n_here, 1, kb, vb, blk_bytes, a.scale_log2);
+    else
+      w.template run<false>(tbl, L, j, j + n_here, 1, kb, vb, blk_bytes, a.scale_log2);
     w.merge_rows_in_wave();
     if (w.row == 0) {
       // (compile-time head loops keep the state in registers)
@@ -462,7 +474,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const AttnAr
   w.reset();
   const int tok0 = p * a.part;
   const int blk_end = (min(tok0 + a.part, L) + B - 1) / B;
-  w.run(a.block_tables + (size_t)s * a.max_blocks_per_seq, L, tok0 / B + wave, blk_end, kWaves,
+  // (rows of one sequence, and partitions, re-read blocks: cached loads)
+  w.template run<false>(a.block_tables + (size_t)s * a.max_blocks_per_seq, L, tok0 / B + wave,
+                        blk_end, kWaves,
         static_cast<const char*>(a.k_cache) + (size_t)g * W::kSliceBytes,
         static_cast<const char*>(a.v_cache) + (size_t)g * W::kSliceBytes,
         (size_t)a.num_kv_heads * W::kSliceBytes, a.scale_log2);

@@ -39,6 +39,7 @@ struct AttnArgs {
   int num_kv_heads;          // Hk
   int group;                 // G = H / Hk
   int max_blocks_per_seq;    // mbs
+  int pool_blocks;           // physical blocks in the K/V pools
   int max_context_len;
   int part;                  // partition length in tokens (multiple of B)
   int max_parts;             // P_max = ceil(max_context_len / part)
