@@ -20,8 +20,9 @@
 //                    (rounded to the input dtype), so nothing moves between
 //                    lanes or through LDS inside the loop.
 //
-// The four waves of a workgroup split the partition's tiles; their (max, sum,
-// O) states are merged through LDS, then written as the final output or as a
+// The four waves of a workgroup split the partition's tiles, each keeping its
+// next tile's loads in flight while it computes one; their (max, sum, O)
+// states are merged through LDS, then written as the final output or as a
 // partition partial for merge_kernel.  fp32: every query row runs the decode
 // kernel over its own visible length.
 #include "pa_common.h"
@@ -148,20 +149,34 @@ __global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a)
   const char* vbase = static_cast<const char*>(a.v_cache);
   const size_t row_bytes = (size_t)D * kElem;
 
-  for (int t0 = tok0 + 32 * wave; t0 < tok_end; t0 += 32 * kWaves) {
-    // this lane loads token t0 + mcol (clamped into the valid range: slots at
-    // or beyond L may hold anything), dims 16 ks + 8 hh .. +7
-    const int t = min(t0 + mcol, L - 1);
-    const int phys = tbl[t / B];
+  // this lane loads token t0 + mcol (clamped into the valid range: slots at
+  // or beyond L may hold anything), dims 16 ks + 8 hh .. +7
+  // A 32-token tile spans 32 / B whole blocks; their ids are read with scalar
+  // loads (a per-lane table read would be a vector load, and waiting for it
+  // would also wait for the tile in flight) and each lane picks its own.
+  static_assert(32 % B == 0, "tiles hold whole blocks");
+  constexpr int kTileBlocks = 32 / B;
+  const ConstI32Ptr tblc = as_const(tbl);
+  const int jlast = (L - 1) / B;
+  auto load_tile = [&](int t0, uint4 (&kr)[KS], uint4 (&vr)[KS]) {
+    const int t = min(t0 + mcol, L - 1);   // >= t0, since t0 < L
+    const int jt = t / B - t0 / B;
+    int phys = tblc[min(t0 / B, jlast)];
+#pragma unroll
+    for (int k = 1; k < kTileBlocks; ++k) {
+      const int id = tblc[min(t0 / B + k, jlast)];
+      phys = (jt == k) ? id : phys;
+    }
     const size_t roff = (((size_t)phys * Hk + g) * B + (t % B)) * row_bytes + hh * 16;
     const uint4* kp = reinterpret_cast<const uint4*>(kbase + roff);
     const uint4* vp = reinterpret_cast<const uint4*>(vbase + roff);
-    uint4 kr[KS], vr[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kr[ks] = kp[2 * ks];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) vr[ks] = vp[2 * ks];
+  };
 
+  auto compute_tile = [&](int t0, const uint4 (&kr)[KS], const uint4 (&vr)[KS]) {
     // S^T = K Q^T: lane holds tokens t0 + tile_token(v, hh) of its row
     f32x16_t sc = f32x16_t{};
 #pragma unroll
@@ -221,6 +236,35 @@ __global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a)
         o[db] = M::mma(va0, pl0, o[db]);
         o[db] = M::mma(va1, pl1, o[db]);
       }
+    }
+  };
+
+  // Software pipeline over two register buffers: the next tile's loads are
+  // issued (in that order, before any of the compute) and stay in flight while
+  // a tile is computed.  The last tile issues nothing, so no load reads past
+  // the wave's range and each wait covers exactly the tile being consumed.
+  constexpr int kStride = 32 * kWaves;
+  int t0 = tok0 + 32 * wave;
+  if (t0 < tok_end) {
+    uint4 k0[KS], v0[KS], k1[KS], v1[KS];
+    load_tile(t0, k0, v0);
+    for (;;) {
+      if (t0 + kStride >= tok_end) {
+        compute_tile(t0, k0, v0);
+        break;
+      }
+      load_tile(t0 + kStride, k1, v1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile(t0, k0, v0);
+      t0 += kStride;
+      if (t0 + kStride >= tok_end) {
+        compute_tile(t0, k1, v1);
+        break;
+      }
+      load_tile(t0 + kStride, k0, v0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile(t0, k1, v1);
+      t0 += kStride;
     }
   }
 
