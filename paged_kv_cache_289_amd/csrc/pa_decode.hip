@@ -414,18 +414,38 @@ __global__ __launch_bounds__(kThreads) void split_merge_kernel(const AttnArgs a)
   const int w0 = a0 / chunk, w1 = (a0 + nb - 1) / chunk;
   if (w0 == w1) return;               // written by its one wave
   const size_t base = (size_t)s * Hk + g;
+  // Pieces are taken eight at a time: the (max, sum, o) loads of a batch are
+  // independent, so a batch costs one memory round trip, and it is folded into
+  // a running log-sum-exp (M, num, den).
+  constexpr int kBatch = 8;
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
     const int h = i / D, d = i % D;
-    float mx = kNegInf;
-    for (int w = w0; w <= w1; ++w) mx = fmaxf(mx, a.ws_ml[2 * ((base + w) * G + h)]);
-    const float ms = (mx == kNegInf) ? 0.f : mx;
-    float num = 0.f, den = 0.f;
-#pragma unroll 4
-    for (int w = w0; w <= w1; ++w) {
-      const size_t sl = (base + w) * G + h;
-      const float wt = fast_exp2(a.ws_ml[2 * sl] - ms);
-      num = __builtin_fmaf(wt, a.ws_o[sl * D + d], num);
-      den = __builtin_fmaf(wt, a.ws_ml[2 * sl + 1], den);
+    float M = kNegInf, num = 0.f, den = 0.f;
+    for (int w = w0; w <= w1; w += kBatch) {
+      float pm[kBatch], pl[kBatch], po[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int wk = min(w + k, w1);   // repeats of the last piece are masked below
+        const size_t sl = (base + wk) * G + h;
+        pm[k] = a.ws_ml[2 * sl];
+        pl[k] = a.ws_ml[2 * sl + 1];
+        po[k] = a.ws_o[sl * D + d];
+      }
+      float mx = M;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (w + k <= w1) mx = fmaxf(mx, pm[k]);
+      const float ms = (mx == kNegInf) ? 0.f : mx;
+      const float r = fast_exp2(M - ms);
+      num *= r;
+      den *= r;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float wt = (w + k <= w1) ? fast_exp2(pm[k] - ms) : 0.f;
+        num = __builtin_fmaf(wt, po[k], num);
+        den = __builtin_fmaf(wt, pl[k], den);
+      }
+      M = mx;
     }
     store_out(a.out, (head0 + h) * D + d, den > 0.f ? num / den : 0.f, a.out_dtype);
   }
