@@ -186,6 +186,21 @@ __device__ inline void group_sum_all(float (&x)[K]) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max / sum of a value and the one held by the lane 32 apart.  v_permlane32_swap
+// exchanges the upper half of one register with the lower half of the other;
+// applied to two copies of x, the two results hold x and its partner in every
+// lane (in some order), so any symmetric combination of them is the answer.
+__device__ inline float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 and leaves the
 // export and LDS/scalar counters unconstrained.
 constexpr int kWaitVmcnt0 = 0x0F70;

@@ -12,7 +12,7 @@
 //   S^T = K Q^T      A = K tile (token x dims), B = Q^T; in the result lane l
 //                    holds 16 of the 32 tokens of row m = l % 32, so the row's
 //                    softmax max/sum is 16 in-lane steps plus one exchange
-//                    with lane l ^ 32.
+//                    with lane l ^ 32 (v_permlane32_swap, no LDS).
 //   V^T = V I        the same 32x32 layout applied to V times an identity:
 //                    lane l receives V at dim 32b + l % 32 for exactly the
 //                    tokens whose probabilities it holds, in the same order.
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a)
         mx = fmaxf(mx, sc[v]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_halves(mx);
     const float m_new = fmaxf(m_run, mx);
     const float ms = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - ms);
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a)
       sc[v] = fast_exp2(sc[v] - ms);
       psum += sc[v];
     }
-    psum += __shfl_xor(psum, 32, 64);
+    psum = sum_halves(psum);
     l_run = __builtin_fmaf(l_run, alpha, psum);
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] *= alpha;
