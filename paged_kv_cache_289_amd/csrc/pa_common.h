@@ -146,6 +146,28 @@ __device__ inline float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
+// Per-lane select: b where the lane's bit of mask is set, else a.
+__device__ inline float lane_select(float a, float b, uint64_t mask) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
+  return r;
+}
+
+// Value of lane n (0..15, a compile-time constant after unrolling) of this
+// lane's 16-lane row (DPP row_newbcast).
+__device__ inline float row_bcast(float x, int n) {
+  switch (n) {
+#define PA_ROW_BCAST(N) \
+    case N: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+    PA_ROW_BCAST(0) PA_ROW_BCAST(1) PA_ROW_BCAST(2) PA_ROW_BCAST(3)
+    PA_ROW_BCAST(4) PA_ROW_BCAST(5) PA_ROW_BCAST(6) PA_ROW_BCAST(7)
+    PA_ROW_BCAST(8) PA_ROW_BCAST(9) PA_ROW_BCAST(10) PA_ROW_BCAST(11)
+    PA_ROW_BCAST(12) PA_ROW_BCAST(13) PA_ROW_BCAST(14) PA_ROW_BCAST(15)
+#undef PA_ROW_BCAST
+    default: return x;
+  }
+}
+
 // Sum over aligned groups of N lanes (N in {1,2,4,8,16,32}); every lane of a
 // group receives the group's sum.  All 64 lanes must be active.
 template <int N>

@@ -69,9 +69,20 @@ struct DecodeWave {
   static constexpr int kSliceBytes = B * kRowBytes;   // one (block, KV head) slice
   static_assert(LPT * EPL == D && TPL * LPT == 64 && LPB * TPL == B, "layout");
 
+  // Weights computed once per row.  When a token row is one 16-lane DPP row,
+  // all 16 lanes of the row hold the same LPB x GP scores after the
+  // all-reduce.  Lane c then evaluates only scores c, c + 16, ... (whose head
+  // is c % GP, as GP divides 16) and the row's weights are broadcast back for
+  // PV.  Each lane keeps the running sum of its own weights (l_lane) against
+  // the max of its head (m_lane); the per-head sums are gathered at the end.
+  static constexpr bool kOwnExp = (LPT == 16);
+  static constexpr int kScores = LPB * GP;
+  static constexpr int kScoresPerLane = (kScores + 15) / 16;
+
   int row, col;                 // token row within a load, 16-byte column
   uint4 qv[GP];
   float m[GP], l[GP], o[GP][EPL];
+  float m_lane, l_lane;         // kOwnExp: this lane's head (col % GP)
 
   __device__ explicit DecodeWave(int lane) : row(lane / LPT), col(lane % LPT) {}
 
@@ -96,6 +107,30 @@ struct DecodeWave {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
     }
+    m_lane = kMaxInit;
+    l_lane = 0.f;
+  }
+
+
+  // the score with index 16 K + c in lane c of each row: four select levels
+  // on c's bits.  The selects are written as v_cndmask instructions: left to
+  // itself the compiler turns the tree into a lane-indexed scratch lookup.
+  // (k is a compile-time constant after unrolling)
+  __device__ float own_score(const float (&sc)[LPB][GP], int k, const uint64_t (&bit)[4]) const {
+    float t0[8], t1[4], t2[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      t0[j] = lane_select(score_at_rt(sc, 16 * k + 2 * j), score_at_rt(sc, 16 * k + 2 * j + 1), bit[0]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t1[j] = lane_select(t0[2 * j], t0[2 * j + 1], bit[1]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) t2[j] = lane_select(t1[2 * j], t1[2 * j + 1], bit[2]);
+    return lane_select(t2[0], t2[1], bit[3]);
+  }
+  // score n of the block (token load n / GP, head n % GP), -inf past the end;
+  // n is a compile-time constant after unrolling
+  __device__ static float score_at_rt(const float (&sc)[LPB][GP], int n) {
+    return n < kScores ? sc[n / GP][n % GP] : kNegInf;
   }
 
   // Blocks j = j_begin, j_begin + step, ... < j_end of the sequence whose table
@@ -122,6 +157,9 @@ struct DecodeWave {
                       const char* kbase, const char* vbase, size_t blk_bytes, float scale_log2) {
     const ConstI32Ptr tbl = as_const(tbl_ptr);
     const float c = exp_scale(scale_log2);
+    uint64_t colbit[4];   // lanes whose column has bit b set (for own_score)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) colbit[b] = __builtin_amdgcn_ballot_w64((col >> b) & 1);
     uint4 kbuf[NBUF][LPB], vbuf[NBUF][LPB];
     auto load_block = [&](int jj, int phys, bool in_range, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
       const int last = min(B - 1, L - 1 - jj * B);   // last valid slot (wave-uniform)
@@ -177,6 +215,7 @@ struct DecodeWave {
         up |= mb[h] > m[h] + kRescaleLog2;
       }
       if (__builtin_amdgcn_ballot_w64(up) != 0) {   // wave-uniform, rare
+        float alpha_lane = 1.f;
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
           const float mn = fmaxf(m[h], mb[h]);
@@ -185,17 +224,37 @@ struct DecodeWave {
           l[h] *= alpha;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+          if (kOwnExp && col % GP == h) {
+            alpha_lane = alpha;
+            m_lane = mn;
+          }
         }
+        l_lane *= alpha_lane;
       }
+      float pf[LPB][GP];   // the weights of the lane's row
+      if constexpr (kOwnExp) {
+        float pk[kScoresPerLane];
 #pragma unroll
-      for (int h = 0; h < GP; ++h) {
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < LPB; ++i) {
-          sc[i][h] = fast_exp2(__builtin_fmaf(sc[i][h], c, -m[h]));
-          psum += sc[i][h];
+        for (int k = 0; k < kScoresPerLane; ++k) {
+          const float sk = own_score(sc, k, colbit);
+          pk[k] = fast_exp2(__builtin_fmaf(sk, c, -m_lane));
+          l_lane += pk[k];
         }
-        l[h] += psum;
+#pragma unroll
+        for (int i = 0; i < LPB; ++i)
+#pragma unroll
+          for (int h = 0; h < GP; ++h) pf[i][h] = row_bcast(pk[(i * GP + h) / 16], (i * GP + h) % 16);
+      } else {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+          float psum = 0.f;
+#pragma unroll
+          for (int i = 0; i < LPB; ++i) {
+            pf[i][h] = fast_exp2(__builtin_fmaf(sc[i][h], c, -m[h]));
+            psum += pf[i][h];
+          }
+          l[h] += psum;
+        }
       }
       // PV: each V element is widened once and used for all GP heads
 #pragma unroll
@@ -205,7 +264,7 @@ struct DecodeWave {
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
 #pragma unroll
-          for (int h = 0; h < GP; ++h) o[h][e] = __builtin_fmaf(sc[i][h], vf[e], o[h][e]);
+          for (int h = 0; h < GP; ++h) o[h][e] = __builtin_fmaf(pf[i][h], vf[e], o[h][e]);
       }
     };
 
@@ -241,6 +300,15 @@ struct DecodeWave {
   // Merge the TPL token rows of the wave (lanes col, col + LPT, ...) by
   // log-sum-exp; afterwards every row holds the wave's state.
   __device__ void merge_rows_in_wave() {
+    if constexpr (kOwnExp) {   // per-head sums from the lanes' own sums
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        float t = 0.f;
+#pragma unroll
+        for (int j = h; j < 16; j += GP) t += row_bcast(l_lane, j);
+        l[h] = t;
+      }
+    }
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
 #pragma unroll
