@@ -162,13 +162,18 @@ int paged_attn_default_partition(int num_seqs, int num_heads, int num_kv_heads, 
                                  int max_context_len, int max_q_len) {
   int part;
   if (max_q_len > 1) {
-    // multi-token queries: one workgroup per (32-row tile, KV head, sequence,
-    // partition); size partitions so that about 2048 workgroups cover the
-    // longest context, in 32-token tiles, between 256 and 4096 tokens
+    // multi-token queries: one workgroup per (row unit, KV head, sequence,
+    // partition), a row unit being one 32-row tile, or four of them when a
+    // sequence has that many rows.  Partitions are sized so that the longest
+    // context is covered by about 2048 workgroups (one-tile units) or 512
+    // (four-tile units: two resident per CU, each doing four times the work),
+    // in 32-token tiles, between 256 and 4096 tokens.
     const int group = num_kv_heads > 0 ? std::max(1, num_heads / num_kv_heads) : 1;
+    const int tiles = ceil_div(max_q_len * group, 32);
+    const bool rows = pa::multiq_rows_mode(max_q_len, group);
     const int64_t units = (int64_t)std::max(1, num_seqs) * std::max(1, num_kv_heads) *
-                          ceil_div(max_q_len * group, 32);
-    int64_t want = (int64_t)max_context_len * units / 2048;
+                          (rows ? ceil_div(tiles, pa::kWaves) : tiles);
+    int64_t want = (int64_t)max_context_len * units / (rows ? 512 : 2048);
     want = std::min<int64_t>(4096, std::max<int64_t>(256, want));
     part = (int)((want + 31) / 32 * 32);
   } else {

@@ -15,6 +15,10 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLog2e = 1.4426950408889634f;
+// Online softmax: the running max moves only when a score beats it by more
+// than this (log2 units), and it starts at a finite sentinel below any score.
+constexpr float kRescaleLog2 = 8.f;
+constexpr float kMaxInit = -1e30f;
 
 // ---------------------------------------------------------------------------
 // element traits: one 16-byte vector = kPerVec elements

@@ -46,8 +46,6 @@ namespace pa {
 #define PA_NBUF 2
 #endif
 constexpr int NBUF = PA_NBUF;   // register ring depth: blocks in flight per wave + 1
-constexpr float kRescaleLog2 = 8.f;
-constexpr float kMaxInit = -1e30f;   // running-max sentinel (below any real score)
 
 // Positive exponent scale for scale_log2 (the sign goes into q, 0 into a tiny
 // value that leaves every weight at exactly 1).
@@ -461,62 +459,65 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
   }
 }
 
-// Merge of one (sequence, KV head) of the split kernel: the waves whose chunks
-// cover its items [a0, a0 + nb) are a0 / chunk .. (a0 + nb - 1) / chunk, and
-// wave w left its piece in slot (s Hk + g + w).  Empty contexts get zero rows.
+// Merge of the split kernel's pieces for one (sequence, query head); thread d
+// owns output dim d.  The items of (s, g) are [a0, a0 + nb) with
+// a0 = Hk pre[s] + g nb, so the waves that covered them are a0 / chunk ..
+// (a0 + nb - 1) / chunk, and wave w left its piece in slot (s Hk + g + w) G + h.
+// Empty contexts get zero rows.  The plan, the length and the prefix sums are
+// read together, then all pieces' (max, sum, o) at once: two memory round
+// trips before the store.
 template <int D>
-__global__ __launch_bounds__(kThreads) void split_merge_kernel(const AttnArgs a) {
-  const int g = blockIdx.x, s = blockIdx.y;
+__global__ __launch_bounds__(D) void split_merge_kernel(const AttnArgs a) {
+  const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   const int H = a.num_heads, Hk = a.num_kv_heads, G = a.group;
-  const int L = min(max(a.context_lens[s], 0), a.max_context_len);
-  const size_t head0 = (size_t)s * H + (size_t)g * G;
-  if (L == 0) {
-    for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-      store_out(a.out, head0 * D + i, 0.f, a.out_dtype);
+  const int g = hq / G, h = hq - g * G;
+  const ConstI32Ptr plan = as_const(a.plan);
+  const int Lraw = as_const(a.context_lens)[s];
+  const int chunk = plan[0];
+  const int p0 = plan[2 + s], p1 = plan[3 + s];
+  const size_t oidx = ((size_t)s * H + hq) * D + d;
+  if (min(max(Lraw, 0), a.max_context_len) == 0) {
+    store_out(a.out, oidx, 0.f, a.out_dtype);
     return;
   }
-  const int chunk = a.plan[0];
-  const int* pre = a.plan + 2;
-  const int nb = pre[s + 1] - pre[s];
-  const int a0 = Hk * pre[s] + g * nb;
+  const int nb = p1 - p0;
+  const int a0 = Hk * p0 + g * nb;
   const int w0 = a0 / chunk, w1 = (a0 + nb - 1) / chunk;
   if (w0 == w1) return;               // written by its one wave
   const size_t base = (size_t)s * Hk + g;
-  // Pieces are taken eight at a time: the (max, sum, o) loads of a batch are
-  // independent, so a batch costs one memory round trip, and it is folded into
-  // a running log-sum-exp (M, num, den).
-  constexpr int kBatch = 8;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int h = i / D, d = i % D;
-    float M = kNegInf, num = 0.f, den = 0.f;
-    for (int w = w0; w <= w1; w += kBatch) {
-      float pm[kBatch], pl[kBatch], po[kBatch];
+  typedef const __attribute__((address_space(4))) float* ConstF32Ptr;
+  const ConstF32Ptr ml = (ConstF32Ptr)a.ws_ml;
+  // Pieces are folded sixteen at a time into a running log-sum-exp (M, num,
+  // den); the loads of a batch are independent.  Past the last piece the index
+  // is clamped and the weight is zero.
+  constexpr int kBatch = 16;
+  float M = kNegInf, num = 0.f, den = 0.f;
+  for (int w = w0; w <= w1; w += kBatch) {
+    float pm[kBatch], pl[kBatch], po[kBatch];
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const int wk = min(w + k, w1);   // repeats of the last piece are masked below
-        const size_t sl = (base + wk) * G + h;
-        pm[k] = a.ws_ml[2 * sl];
-        pl[k] = a.ws_ml[2 * sl + 1];
-        po[k] = a.ws_o[sl * D + d];
-      }
-      float mx = M;
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k)
-        if (w + k <= w1) mx = fmaxf(mx, pm[k]);
-      const float ms = (mx == kNegInf) ? 0.f : mx;
-      const float r = fast_exp2(M - ms);
-      num *= r;
-      den *= r;
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const float wt = (w + k <= w1) ? fast_exp2(pm[k] - ms) : 0.f;
-        num = __builtin_fmaf(wt, po[k], num);
-        den = __builtin_fmaf(wt, pl[k], den);
-      }
-      M = mx;
+    for (int k = 0; k < kBatch; ++k) {
+      const size_t sl = (base + min(w + k, w1)) * G + h;
+      pm[k] = ml[2 * sl];
+      pl[k] = ml[2 * sl + 1];
+      po[k] = a.ws_o[sl * D + d];
     }
-    store_out(a.out, (head0 + h) * D + d, den > 0.f ? num / den : 0.f, a.out_dtype);
+    float mx = M;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (w + k <= w1) mx = fmaxf(mx, pm[k]);
+    const float ms = (mx == kNegInf) ? 0.f : mx;
+    const float r = fast_exp2(M - ms);
+    num *= r;
+    den *= r;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float wt = (w + k <= w1) ? fast_exp2(pm[k] - ms) : 0.f;
+      num = __builtin_fmaf(wt, po[k], num);
+      den = __builtin_fmaf(wt, pl[k], den);
+    }
+    M = mx;
   }
+  store_out(a.out, oidx, den > 0.f ? num / den : 0.f, a.out_dtype);
 }
 
 // ---------------------------------------------------------------------------
@@ -699,8 +700,7 @@ static hipError_t launch_decode_t(int num_seqs, const AttnArgs& a, hipStream_t s
     hipError_t e = hipGetLastError();
     if (ev.stop) (void)hipEventRecord(ev.stop, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((split_merge_kernel<D>), dim3(a.num_kv_heads, num_seqs), dim3(kThreads),
-                       0, st, a);
+    hipLaunchKernelGGL((split_merge_kernel<D>), dim3(a.num_heads, num_seqs), dim3(D), 0, st, a);
     return hipGetLastError();
   }
   // per-row mode launches one grid row per (sequence, query row) slot

@@ -18,6 +18,13 @@ namespace pa {
 constexpr int kWaves = PA_WAVES;
 constexpr int kThreads = 64 * kWaves;
 
+// Multi-token queries: a workgroup takes four 32-row tiles of one (sequence,
+// KV head) over the same K/V tiles when a sequence can have that many rows
+// (n * G > 96); otherwise it takes one row tile and splits the tokens.
+inline bool multiq_rows_mode(int max_q_len, int group) {
+  return (max_q_len * group + 31) / 32 >= kWaves;
+}
+
 // Balanced-split decode: most sequences per call it handles (their prefix sums
 // live in LDS), and most waves it launches (the workspace is sized for this).
 constexpr int kMaxSplitSeqs = 8192;

@@ -33,6 +33,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+
 template <int DT> struct Mma;
 
 template <> struct Mma<PA_BF16> {
@@ -41,9 +45,13 @@ template <> struct Mma<PA_BF16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
-  // two floats -> two bf16 (round to nearest even), lo in the low half
+  // two floats -> two bf16 rounded to nearest even (v_cvt_pk_bf16_f32), lo in the low half
   __device__ static inline uint32_t pack2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{lo, hi}, bf16x2v_t));
+  }
+  // two floats that are bf16 values already: their upper halves (exact)
+  __device__ static inline uint32_t pack2_exact(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
   }
 };
 
@@ -54,16 +62,13 @@ template <> struct Mma<PA_F16> {
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
   }
   __device__ static inline uint32_t pack2(float lo, float hi) {
-    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{lo, hi}, f16x2v_t));
+  }
+  // two floats that are f16 values already (rounding toward zero changes nothing)
+  __device__ static inline uint32_t pack2_exact(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
   }
 };
-
-// x rounded to the nearest bf16, as a float
-__device__ inline float bf16_round(float x) {
-  return __uint_as_float((uint32_t)f32_to_bf16_rne(x) << 16);
-}
 
 template <int DT>
 __device__ inline uint4 pack8(const f32x16_t& x, int base) {
@@ -72,23 +77,52 @@ __device__ inline uint4 pack8(const f32x16_t& x, int base) {
                     M::pack2(x[base + 4], x[base + 5]), M::pack2(x[base + 6], x[base + 7]));
 }
 
+template <int DT>
+__device__ inline uint4 pack8_exact(const f32x16_t& x, int base) {
+  using M = Mma<DT>;
+  return make_uint4(M::pack2_exact(x[base + 0], x[base + 1]), M::pack2_exact(x[base + 2], x[base + 3]),
+                    M::pack2_exact(x[base + 4], x[base + 5]), M::pack2_exact(x[base + 6], x[base + 7]));
+}
+
 // token offset (within a 32-token tile) of C-layout register v in lane half hh
 __device__ constexpr int tile_token(int v, int hh) { return 8 * (v / 4) + 4 * hh + (v % 4); }
 
-template <int DT, int D, int B>
-__global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a) {
+// ROWS = false: one 32-row tile per workgroup; its four waves take
+//   interleaved 32-token tiles of the partition (each staging its own tiles
+//   through its own LDS area) and merge through LDS at the end.
+// ROWS = true:  four row tiles per workgroup, one per wave, over the same
+//   tokens; the 256 threads stage each K/V tile once into a double-buffered LDS
+//   area that all four waves read.  Used when a sequence has many query rows
+//   (prefill chunks), where it cuts the K/V traffic per row by four.
+//
+// Staging: a K or V tile is 32 token rows of D elements.  Thread c of the
+// stagers loads 16-byte chunks c, c + NP, ... in memory order (a wave reads
+// four whole rows, 1 KiB, per instruction) and writes them to LDS rows padded
+// by 16 bytes, from which each lane reads its MFMA operands (row = token
+// mcol, 16 bytes per k-step) without bank conflicts.
+template <int DT, int D, int B, bool ROWS>
+__device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
   using M = Mma<DT>;
   constexpr int KS = D / 16;   // k-steps of QK over head_dim
   constexpr int DB = D / 32;   // 32-dim blocks of the output
   constexpr int kElem = 2;
+  constexpr int kRowBytes = D * kElem;
+  constexpr int RS = kRowBytes + 16;       // LDS row stride in bytes
+  constexpr int kTileBytes = 32 * RS;      // one K or V tile in LDS
+  constexpr int CPR = kRowBytes / 16;      // 16-byte chunks per token row
+  constexpr int NP = ROWS ? kThreads : 64; // threads staging one tile
+  constexpr int kPer = 32 * CPR / NP;      // chunks per staging thread per tensor
+  static_assert(kPer * NP == 32 * CPR && NP % CPR == 0, "staging layout");
 
   const int G = a.group, H = a.num_heads, Hk = a.num_kv_heads;
   const int g = blockIdx.y, s = blockIdx.z;
   const int rt_count = (a.max_q_len * G + 31) / 32;
-  const int rt = blockIdx.x % rt_count, p = blockIdx.x / rt_count;
+  const int units = ROWS ? (rt_count + kWaves - 1) / kWaves : rt_count;
+  const int ux = blockIdx.x % units, p = blockIdx.x / units;
   const int q0 = a.q_offsets[s], n = a.q_offsets[s + 1] - q0;
   const int n_rows = n * G;
-  if (rt * 32 >= n_rows) return;
+  const int wg_row0 = (ROWS ? ux * kWaves : ux) * 32;
+  if (wg_row0 >= n_rows) return;       // workgroup-uniform
   const int L = min(max(a.context_lens[s], 0), a.max_context_len);
 
   const int tid = threadIdx.x;
@@ -96,27 +130,32 @@ __global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;            // lane half: which 16 of a tile's 32 tokens
   const int mcol = lane & 31;          // this lane's query row within the tile
+  const int rt = ROWS ? ux * kWaves + wave : ux;
+  const bool wave_rows = rt * 32 < n_rows;   // (ROWS: a wave past the rows only stages)
   const int r = rt * 32 + mcol;
-  const bool row_ok = r < n_rows;
+  const bool row_ok = wave_rows && r < n_rows;
   const int qi = row_ok ? r / G : 0;   // query token of the row
   const int qh = row_ok ? r % G : 0;   // head within the group
-  // visible keys of this row, and of the tile's last (most-seeing) row
-  const int lrow = !row_ok ? 0 : (a.causal ? max(0, min(L, L - n + qi + 1)) : L);
-  const int last_i = (min(rt * 32 + 31, n_rows - 1)) / G;
-  const int first_i = (rt * 32) / G;
-  const int l_tile_max = a.causal ? max(0, min(L, L - n + last_i + 1)) : L;
-  const int l_tile_min = a.causal ? max(0, min(L, L - n + first_i + 1)) : L;
+  auto visible = [&](int i) { return a.causal ? max(0, min(L, L - n + i + 1)) : L; };
+  // visible keys of this row, of the wave's first and last rows, and of the
+  // workgroup's last (most-seeing) row
+  const int lrow = row_ok ? visible(qi) : 0;
+  const int l_tile_max = wave_rows ? visible(min(rt * 32 + 31, n_rows - 1) / G) : 0;
+  const int l_tile_min = wave_rows ? visible((rt * 32) / G) : 0;
+  const int wg_rows = ROWS ? 32 * kWaves : 32;
+  const int l_wg_max = visible(min(wg_row0 + wg_rows - 1, n_rows - 1) / G);
   const int parts_row = (lrow + a.part - 1) / a.part;
   const size_t out_row = ((size_t)(q0 + qi) * H + (size_t)g * G + qh);   // (token, head) index
 
   const int tok0 = p * a.part;
   if (L == 0) {  // nothing visible: zero rows, written once
-    if (p == 0 && wave == 0 && row_ok)
+    if (p == 0 && (ROWS || wave == 0) && row_ok)
       for (int d = hh * (D / 2); d < (hh + 1) * (D / 2); ++d) store_out(a.out, out_row * D + d, 0.f, a.out_dtype);
     return;
   }
-  if (tok0 >= l_tile_max) return;      // no row of this tile sees this partition
-  const int tok_end = min(tok0 + a.part, l_tile_max);
+  if (tok0 >= l_wg_max) return;        // no row of this workgroup sees this partition
+  const int wg_end = min(tok0 + a.part, l_wg_max);
+  const int tok_end = min(tok0 + a.part, l_tile_max);   // this wave's keys end here
   const int lim = min(lrow, tok_end);  // this lane-row's keys end here (within the partition)
 
   // Q^T operand: row m = lane % 32, dims 16 ks + 8 hh .. +7
@@ -125,7 +164,17 @@ __global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a)
     const uint4* qp = reinterpret_cast<const uint4*>(a.q) + (out_row * D + hh * 8) / 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qv[ks] = row_ok ? qp[2 * ks] : make_uint4(0, 0, 0, 0);
+    // a negative scale goes into q's sign bits (exact), so the scores are
+    // scaled by a positive c inside the exponent's FMA
+    if (a.scale_log2 < 0.f) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qv[ks].x ^= 0x80008000u; qv[ks].y ^= 0x80008000u;
+        qv[ks].z ^= 0x80008000u; qv[ks].w ^= 0x80008000u;
+      }
+    }
   }
+  const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
   // identity operands selecting dims 0..15 and 16..31 of a 32-dim block
   uint4 eye[2];
 #pragma unroll
@@ -142,38 +191,61 @@ __global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a)
   f32x16_t o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
-  float m_run = kNegInf, l_run = 0.f;
+  // running max (log2 units) starts at a finite sentinel below any score, so
+  // rows that see no key stay free of inf - inf
+  float m_run = kMaxInit, l_run = 0.f;
 
-  const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
-  const size_t row_bytes = (size_t)D * kElem;
 
-  // this lane loads token t0 + mcol (clamped into the valid range: slots at
-  // or beyond L may hold anything), dims 16 ks + 8 hh .. +7
   // A 32-token tile spans 32 / B whole blocks; their ids are read with scalar
-  // loads (a per-lane table read would be a vector load, and waiting for it
-  // would also wait for the tile in flight) and each lane picks its own.
+  // loads and each staging lane picks the one of its token.  Tokens at or past
+  // L are clamped to the last valid one (their slots may hold anything) and
+  // masked in the scores.
   static_assert(32 % B == 0, "tiles hold whole blocks");
   constexpr int kTileBlocks = 32 / B;
-  const ConstI32Ptr tblc = as_const(tbl);
+  const ConstI32Ptr tblc = as_const(a.block_tables + (size_t)s * a.max_blocks_per_seq);
   const int jlast = (L - 1) / B;
-  auto load_tile = [&](int t0, uint4 (&kr)[KS], uint4 (&vr)[KS]) {
-    const int t = min(t0 + mcol, L - 1);   // >= t0, since t0 < L
-    const int jt = t / B - t0 / B;
-    int phys = tblc[min(t0 / B, jlast)];
+  // Staged chunks are held as a native vector type: copies of the uint4 struct
+  // between global memory and LDS would pass through private memory.
+  const int spid = ROWS ? tid : lane;  // this thread's staging index
+  const int scol = spid % CPR;         // its 16-byte column
+  auto stage_load = [&](int t0, u32x4_t (&sk)[kPer], u32x4_t (&sv)[kPer]) {
+    int ids[kTileBlocks];
 #pragma unroll
-    for (int k = 1; k < kTileBlocks; ++k) {
-      const int id = tblc[min(t0 / B + k, jlast)];
-      phys = (jt == k) ? id : phys;
+    for (int k = 0; k < kTileBlocks; ++k) ids[k] = tblc[min(t0 / B + k, jlast)];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int tok = spid / CPR + i * (NP / CPR);
+      const int t = min(t0 + tok, L - 1);   // >= t0, since t0 < L
+      const int jt = t / B - t0 / B;
+      int phys = ids[0];
+#pragma unroll
+      for (int k = 1; k < kTileBlocks; ++k) phys = (jt == k) ? ids[k] : phys;
+      const size_t off = (((size_t)phys * Hk + g) * B + (t % B)) * kRowBytes + scol * 16;
+      sk[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
+      sv[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
     }
-    const size_t roff = (((size_t)phys * Hk + g) * B + (t % B)) * row_bytes + hh * 16;
-    const uint4* kp = reinterpret_cast<const uint4*>(kbase + roff);
-    const uint4* vp = reinterpret_cast<const uint4*>(vbase + roff);
+  };
+  constexpr int kLdsBytes = ROWS ? 2 * 2 * kTileBytes : 16;   // (only the rows layout stages)
+  __shared__ __attribute__((aligned(16))) char sm_kv[kLdsBytes];
+  // base: K tile, base + kTileBytes: V tile
+  auto stage_store = [&](char* base, const u32x4_t (&sk)[kPer], const u32x4_t (&sv)[kPer]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kr[ks] = kp[2 * ks];
+    for (int i = 0; i < kPer; ++i) {
+      const int tok = spid / CPR + i * (NP / CPR);
+      *reinterpret_cast<u32x4_t*>(base + tok * RS + scol * 16) = sk[i];
+      *reinterpret_cast<u32x4_t*>(base + kTileBytes + tok * RS + scol * 16) = sv[i];
+    }
+  };
+  // this lane's operands: token mcol, dims 16 ks + 8 hh .. +7
+  auto lds_read = [&](const char* base, uint4 (&kr)[KS], uint4 (&vr)[KS]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) vr[ks] = vp[2 * ks];
+    for (int ks = 0; ks < KS; ++ks)
+      kr[ks] = *reinterpret_cast<const uint4*>(base + mcol * RS + 32 * ks + 16 * hh);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      vr[ks] = *reinterpret_cast<const uint4*>(base + kTileBytes + mcol * RS + 32 * ks + 16 * hh);
   };
 
   auto compute_tile = [&](int t0, const uint4 (&kr)[KS], const uint4 (&vr)[KS]) {
@@ -185,51 +257,59 @@ __global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a)
     float mx = kNegInf;
     if (t0 + 32 <= min(l_tile_min, tok_end)) {   // wave-uniform: no key of the tile is masked
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        sc[v] *= a.scale_log2;
-        mx = fmaxf(mx, sc[v]);
-      }
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
     } else {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        sc[v] = (t0 + tile_token(v, hh) < lim) ? sc[v] * a.scale_log2 : kNegInf;
+        sc[v] = (t0 + tile_token(v, hh) < lim) ? sc[v] : kNegInf;
         mx = fmaxf(mx, sc[v]);
       }
     }
-    mx = max_halves(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float ms = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - ms);
-    m_run = m_new;
+    mx = max_halves(mx) * c;   // the row's tile max in log2 units (c > 0)
+    // Lazy rescaling: the running max moves only when a score beats it by
+    // more than kRescaleLog2; otherwise the weights are taken against the
+    // stale max (so they are at most 2^kRescaleLog2) and o, l keep their scale.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {   // wave-uniform
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      sc[v] = fast_exp2(sc[v] - ms);
+      sc[v] = fast_exp2(__builtin_fmaf(sc[v], c, -m_run));
       psum += sc[v];
     }
-    psum = sum_halves(psum);
-    l_run = __builtin_fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    l_run += sum_halves(psum);
 
     // P^T operands.  bf16 keeps 8 significant bits, too few for the
-    // probabilities at short contexts, so P is split into a bf16 head and a bf16
-    // residual (p = hi + lo to about 2^-17) and both are multiplied; f16's 11
-    // bits are used as they are.
-    const uint4 pb0 = pack8<DT>(sc, 0), pb1 = pack8<DT>(sc, 8);
-    uint4 pl0, pl1;
+    // probabilities at short contexts, so P is split into a head (p with its
+    // low 16 bits cleared, exact) and the residual p - head (exact in fp32,
+    // then rounded to bf16), and both are multiplied: p is carried to about
+    // 2^-16.  f16's 11 bits are used as they are (rounded to nearest).
+    uint4 pb0, pb1, pl0, pl1;
     if constexpr (DT == PA_BF16) {
       f32x16_t res;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) res[v] = sc[v] - bf16_round(sc[v]);
+      for (int v = 0; v < 16; ++v)
+        res[v] = sc[v] - __uint_as_float(__float_as_uint(sc[v]) & 0xffff0000u);
+      pb0 = pack8_exact<DT>(sc, 0);
+      pb1 = pack8_exact<DT>(sc, 8);
       pl0 = pack8<DT>(res, 0);
       pl1 = pack8<DT>(res, 8);
+    } else {
+      pb0 = pack8<DT>(sc, 0);
+      pb1 = pack8<DT>(sc, 8);
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
+      // V I reproduces the V values exactly, so repacking them is exact
       f32x16_t vt = M::mma(vr[2 * db], eye[0], f32x16_t{});
       vt = M::mma(vr[2 * db + 1], eye[1], vt);
-      const uint4 va0 = pack8<DT>(vt, 0), va1 = pack8<DT>(vt, 8);
+      const uint4 va0 = pack8_exact<DT>(vt, 0), va1 = pack8_exact<DT>(vt, 8);
       o[db] = M::mma(va0, pb0, o[db]);
       o[db] = M::mma(va1, pb1, o[db]);
       if constexpr (DT == PA_BF16) {
@@ -239,66 +319,120 @@ __global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a)
     }
   };
 
-  // Software pipeline over two register buffers: the next tile's loads are
-  // issued (in that order, before any of the compute) and stay in flight while
-  // a tile is computed.  The last tile issues nothing, so no load reads past
-  // the wave's range and each wait covers exactly the tile being consumed.
-  constexpr int kStride = 32 * kWaves;
-  int t0 = tok0 + 32 * wave;
-  if (t0 < tok_end) {
-    uint4 k0[KS], v0[KS], k1[KS], v1[KS];
-    load_tile(t0, k0, v0);
-    for (;;) {
-      if (t0 + kStride >= tok_end) {
+  if constexpr (ROWS) {
+    // All four waves walk the workgroup's tiles [tok0, wg_end) in step: tile
+    // i is read from LDS buffer i % 2 while tile i + 1 is loaded into
+    // registers and then stored to the other buffer; one barrier per tile.
+    // The loop bounds are workgroup-uniform, so every wave reaches every
+    // barrier, and the last tile is peeled off so that every load in the loop
+    // is unconditional.
+    auto compute_from = [&](int t0, const char* base) {
+      if (t0 < tok_end) {   // wave-uniform: the wave's rows see keys in this tile
+        uint4 kr[KS], vr[KS];
+        lds_read(base, kr, vr);
+        compute_tile(t0, kr, vr);
+      }
+    };
+    int t0 = tok0;
+    int buf = 0;
+    u32x4_t sk[kPer], sv[kPer];
+    stage_load(t0, sk, sv);
+    stage_store(sm_kv, sk, sv);
+    __syncthreads();
+    while (t0 + 32 < wg_end) {
+      stage_load(t0 + 32, sk, sv);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_from(t0, sm_kv + buf * 2 * kTileBytes);
+      buf ^= 1;
+      stage_store(sm_kv + buf * 2 * kTileBytes, sk, sv);
+      __syncthreads();
+      t0 += 32;
+    }
+    compute_from(t0, sm_kv + buf * 2 * kTileBytes);
+  } else {
+    // Each wave takes tiles tok0 + 32 wave, + 32 kWaves, ... and loads them
+    // straight into registers in the operand layout (lane (mcol, hh) reads
+    // token t0 + mcol, 16 bytes per k-step).  Two register buffers: the next
+    // tile's loads are issued (K, then V, before any of the compute) and stay
+    // in flight while a tile is computed; the last tile issues nothing, so
+    // each wait covers exactly the tile being consumed.
+    auto load_tile = [&](int t0, uint4 (&kr)[KS], uint4 (&vr)[KS]) {
+      const int t = min(t0 + mcol, L - 1);   // >= t0, since t0 < L
+      const int jt = t / B - t0 / B;
+      int phys = tblc[min(t0 / B, jlast)];
+#pragma unroll
+      for (int k = 1; k < kTileBlocks; ++k) {
+        const int id = tblc[min(t0 / B + k, jlast)];
+        phys = (jt == k) ? id : phys;
+      }
+      const size_t roff = (((size_t)phys * Hk + g) * B + (t % B)) * kRowBytes + hh * 16;
+      const uint4* kp = reinterpret_cast<const uint4*>(kbase + roff);
+      const uint4* vp = reinterpret_cast<const uint4*>(vbase + roff);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kr[ks] = kp[2 * ks];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) vr[ks] = vp[2 * ks];
+    };
+    constexpr int kStride = 32 * kWaves;
+    int t0 = tok0 + 32 * wave;
+    if (t0 < tok_end) {
+      uint4 k0[KS], v0[KS], k1[KS], v1[KS];
+      load_tile(t0, k0, v0);
+      for (;;) {
+        if (t0 + kStride >= tok_end) {
+          compute_tile(t0, k0, v0);
+          break;
+        }
+        load_tile(t0 + kStride, k1, v1);
+        __builtin_amdgcn_sched_barrier(0);
         compute_tile(t0, k0, v0);
-        break;
-      }
-      load_tile(t0 + kStride, k1, v1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_tile(t0, k0, v0);
-      t0 += kStride;
-      if (t0 + kStride >= tok_end) {
+        t0 += kStride;
+        if (t0 + kStride >= tok_end) {
+          compute_tile(t0, k1, v1);
+          break;
+        }
+        load_tile(t0 + kStride, k0, v0);
+        __builtin_amdgcn_sched_barrier(0);
         compute_tile(t0, k1, v1);
-        break;
+        t0 += kStride;
       }
-      load_tile(t0 + kStride, k0, v0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_tile(t0, k1, v1);
-      t0 += kStride;
     }
   }
 
-  // merge the waves' states through LDS, one wave at a time, into wave 0
-  __shared__ float sm_o[32][D + 4];
-  __shared__ float sm_m[32], sm_l[32];
-  for (int w = 1; w < kWaves; ++w) {
-    if (wave == w) {
+  if constexpr (!ROWS) {
+    // merge the waves' states through LDS, one wave at a time, into wave 0
+    __shared__ float sm_o[32][D + 4];
+    __shared__ float sm_m[32], sm_l[32];
+    for (int w = 1; w < kWaves; ++w) {
+      if (wave == w) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sm_o[mcol][32 * db + tile_token(v, hh)] = o[db][v];
-      if (hh == 0) {
-        sm_m[mcol] = m_run;
-        sm_l[mcol] = l_run;
+          for (int v = 0; v < 16; ++v) sm_o[mcol][32 * db + tile_token(v, hh)] = o[db][v];
+        if (hh == 0) {
+          sm_m[mcol] = m_run;
+          sm_l[mcol] = l_run;
+        }
       }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const float m2 = sm_m[mcol], l2 = sm_l[mcol];
-      const float mxw = fmaxf(m_run, m2);
-      const float ms = (mxw == kNegInf) ? 0.f : mxw;
-      const float a1 = fast_exp2(m_run - ms), a2 = fast_exp2(m2 - ms);
-      l_run = l_run * a1 + l2 * a2;
-      m_run = mxw;
+      __syncthreads();
+      if (wave == 0) {
+        const float m2 = sm_m[mcol], l2 = sm_l[mcol];
+        const float mxw = fmaxf(m_run, m2);
+        const float ms = (mxw == kNegInf) ? 0.f : mxw;
+        const float a1 = fast_exp2(m_run - ms), a2 = fast_exp2(m2 - ms);
+        l_run = l_run * a1 + l2 * a2;
+        m_run = mxw;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          o[db][v] = o[db][v] * a1 + sm_o[mcol][32 * db + tile_token(v, hh)] * a2;
+          for (int v = 0; v < 16; ++v)
+            o[db][v] = o[db][v] * a1 + sm_o[mcol][32 * db + tile_token(v, hh)] * a2;
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    if (wave != 0) return;
   }
-  if (wave != 0 || !row_ok) return;
+  if (!row_ok) return;
 
   // lane (mcol, hh) holds dims 32 db + 8 c + 4 hh + (0..3) of its row
   if (parts_row <= 1) {
@@ -325,15 +459,33 @@ __global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a)
   }
 }
 
+// The two layouts as kernels.  The rows layout fits two waves per SIMD
+// (it holds one staged chunk per thread instead of two register tiles per
+// wave), which lets one wave's softmax overlap the other's matrix products.
+template <int DT, int D, int B>
+__global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a) {
+  multiq_mfma_body<DT, D, B, false>(a);
+}
+
+template <int DT, int D, int B>
+__global__ __launch_bounds__(kThreads, 2) void multiq_mfma_rows_kernel(const AttnArgs a) {
+  multiq_mfma_body<DT, D, B, true>(a);
+}
+
 hipError_t launch_merge(int head_dim, int num_seqs, const AttnArgs& a, hipStream_t st);
 
 template <int DT, int D, int B>
 static hipError_t launch_mfma_t(int num_seqs, const AttnArgs& a, hipStream_t st,
                                 const KernelEvents& ev) {
   const int rt_count = (a.max_q_len * a.group + 31) / 32;
-  dim3 grid(rt_count * a.max_parts, a.num_kv_heads, num_seqs);
+  const bool rows = multiq_rows_mode(a.max_q_len, a.group);
+  const int units = rows ? (rt_count + kWaves - 1) / kWaves : rt_count;
+  dim3 grid(units * a.max_parts, a.num_kv_heads, num_seqs);
   if (ev.start) (void)hipEventRecord(ev.start, st);
-  hipLaunchKernelGGL((multiq_mfma_kernel<DT, D, B>), grid, dim3(kThreads), 0, st, a);
+  if (rows)
+    hipLaunchKernelGGL((multiq_mfma_rows_kernel<DT, D, B>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((multiq_mfma_kernel<DT, D, B>), grid, dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (ev.stop) (void)hipEventRecord(ev.stop, st);
   if (e != hipSuccess || a.max_parts <= 1) return e;

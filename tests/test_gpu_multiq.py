@@ -60,6 +60,44 @@ def test_multiq_shapes(dtype, D, B, G):
         U.assert_close(out, want, dtype, f"part={part}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B", [8, 16, 32])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_multiq_many_rows(dtype, D, B, G):
+    """More than 96 query rows per KV head (n * G > 96): a workgroup takes four 32-row
+    tiles over the same staged K/V tiles.  Row counts are ragged, so some workgroups
+    have waves without rows; partitions that are not multiples of the 32-token tile
+    make tiles straddle partition ends."""
+    q_len_max = {1: 200, 4: 50, 8: 25}[G]
+    st = W.random_small(3000 + G * 7 + B + D, num_seqs=4, num_heads=2 * G, num_kv_heads=2,
+                        head_dim=D, block_size=B, ctx_lo=q_len_max, ctx_hi=520,
+                        q_len_max=q_len_max, dtype=dtype)
+    U.say(f"multiq rows {dtype} D={D} B={B} G={G} ctx={list(st.context_lens)} "
+          f"n={list(st.q_lens)}")
+    vals = W.host_values(st)
+    t = U.upload(st, vals)
+    for causal in (True, False):
+        want = U.oracle_multiq(st, vals, causal=causal)
+        for part in (0, 32, 3 * B if B < 32 else 64):
+            out = U.run_multiq(st, t, causal=causal, out_dtype=torch.float32,
+                               partition_tokens=part)
+            U.assert_close(out, want, dtype, f"causal={causal} part={part}")
+    out = U.run_multiq(st, t)
+    U.assert_close(out, U.oracle_multiq(st, vals), dtype, f"out {dtype}")
+
+
+def test_multiq_many_rows_poison_and_determinism():
+    st = W.chunked_prefill(7, cached=200, chunk=40)
+    vals = W.host_values(st)
+    a = U.run_multiq(st, U.upload(st, vals), partition_tokens=64)
+    b = U.run_multiq(st, U.upload(st, W.poison_unused(st, vals)), partition_tokens=64)
+    c = U.run_multiq(st, U.upload(st, vals), partition_tokens=64)
+    assert np.all(np.isfinite(U.to_f64(b)))
+    assert np.array_equal(U.bits(a), U.bits(b))
+    assert np.array_equal(U.bits(a), U.bits(c))
+
+
 def test_multiq_with_one_row_equals_decode():
     st = W.llama3_8b_decode(3, num_seqs=6, ctx_lo=1, ctx_hi=700)
     vals = W.host_values(st)
