@@ -615,61 +615,68 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const AttnAr
   }
 }
 
-// Log-sum-exp merge of the partitions of one (row, KV-head group):
-// M = max_p m_p, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
-// The loads of different partitions are independent, so the loops are unrolled
-// to keep several in flight.
+// Log-sum-exp merge of the partitions of one (row, query head); thread d owns
+// output dim d: M = max_p m_p, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// Rows with a single partition were finished by the partial kernel.  The
+// length (and the row's place in its sequence) is read first, then every
+// partition's (max, sum, o) in batches of independent loads.
 template <int D>
-__device__ inline void merge_rows(const AttnArgs& a, size_t row, int g, int n_parts) {
-  const int H = a.num_heads, G = a.group;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int h = i / D, d = i % D;
-    const size_t hh = row * H + (size_t)g * G + h;
-    const float* ml = a.ws_ml + 2 * hh * a.max_parts;
-    const float* po = a.ws_o + hh * a.max_parts * D + d;
-    float mx = kNegInf;
-#pragma unroll 8
-    for (int p = 0; p < n_parts; ++p) mx = fmaxf(mx, ml[2 * p]);
-    const float ms = (mx == kNegInf) ? 0.f : mx;
-    float num = 0.f, den = 0.f;
-#pragma unroll 8
-    for (int p = 0; p < n_parts; ++p) {
-      const float wt = fast_exp2(ml[2 * p] - ms);
-      num = __builtin_fmaf(wt, po[(size_t)p * D], num);
-      den = __builtin_fmaf(wt, ml[2 * p + 1], den);
-    }
-    store_out(a.out, hh * D + d, den > 0.f ? num / den : 0.f, a.out_dtype);
-  }
-}
-
-// Merge of the partition kernel's (and the multi-query kernel's) partials.
-// Rows with a single partition were finished by the partition kernel.
-template <int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(const AttnArgs a) {
-  const int g = blockIdx.y, s = blockIdx.z;
+__global__ __launch_bounds__(D) void merge_kernel(const AttnArgs a) {
+  const int hq = blockIdx.x, s = blockIdx.z, d = threadIdx.x;
   size_t row = s;
   int L = min(max(a.context_lens[s], 0), a.max_context_len);
-  if (a.q_offsets) {  // multi-token queries: blockIdx.x = row within the sequence
+  if (a.q_offsets) {  // multi-token queries: blockIdx.y = row within the sequence
     const int q0 = a.q_offsets[s], n = a.q_offsets[s + 1] - q0;
-    const int i = blockIdx.x;
+    const int i = blockIdx.y;
     if (i >= n) return;
     row = (size_t)q0 + i;
     if (a.causal) L = max(0, min(L, L - n + i + 1));
   }
   const int n_parts = (L + a.part - 1) / a.part;
   if (n_parts <= 1) return;
-  merge_rows<D>(a, row, g, n_parts);
+  const size_t hh = row * a.num_heads + hq;
+  typedef const __attribute__((address_space(4))) float* ConstF32Ptr;
+  const ConstF32Ptr ml = (ConstF32Ptr)(a.ws_ml + 2 * hh * a.max_parts);
+  const float* po = a.ws_o + hh * a.max_parts * D + d;
+  constexpr int kBatch = 16;
+  float M = kNegInf, num = 0.f, den = 0.f;
+  for (int p0 = 0; p0 < n_parts; p0 += kBatch) {
+    float pm[kBatch], pl[kBatch], pv[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int pk = min(p0 + k, n_parts - 1);   // repeats past the end get weight 0
+      pm[k] = ml[2 * pk];
+      pl[k] = ml[2 * pk + 1];
+      pv[k] = po[(size_t)pk * D];
+    }
+    float mx = M;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (p0 + k < n_parts) mx = fmaxf(mx, pm[k]);
+    const float ms = (mx == kNegInf) ? 0.f : mx;
+    const float r = fast_exp2(M - ms);
+    num *= r;
+    den *= r;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float wt = (p0 + k < n_parts) ? fast_exp2(pm[k] - ms) : 0.f;
+      num = __builtin_fmaf(wt, pv[k], num);
+      den = __builtin_fmaf(wt, pl[k], den);
+    }
+    M = mx;
+  }
+  store_out(a.out, hh * D + d, den > 0.f ? num / den : 0.f, a.out_dtype);
 }
 
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
 hipError_t launch_merge(int head_dim, int num_seqs, const AttnArgs& a, hipStream_t st) {
-  dim3 mgrid(a.q_offsets ? a.max_q_len : 1, a.num_kv_heads, num_seqs);
+  dim3 mgrid(a.num_heads, a.q_offsets ? a.max_q_len : 1, num_seqs);
   if (head_dim == 64)
-    hipLaunchKernelGGL((merge_kernel<64>), mgrid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((merge_kernel<64>), mgrid, dim3(64), 0, st, a);
   else
-    hipLaunchKernelGGL((merge_kernel<128>), mgrid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((merge_kernel<128>), mgrid, dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
