@@ -160,9 +160,10 @@ int paged_attn_check_inputs(const int32_t* block_tables, const int32_t* context_
 /*
  * Profiling aid.  With both arguments non-NULL (hipEvent_t handles), every
  * later paged_attn_decode / paged_attn_multiq call made from this host thread
- * records `start` on its stream right before its main kernel and `stop` right
- * after it (a partition merge, if any, runs after `stop`), so the elapsed time
- * between them is that kernel's duration.  NULL, NULL turns it off.  The
+ * launches its main kernel with hipExtLaunchKernel, which stamps `start` and
+ * `stop` with that dispatch's own start and end on the call's stream (a
+ * partition merge, if any, runs after `stop`), so the elapsed time between
+ * them is that kernel's duration.  NULL, NULL turns it off.  The
  * events are caller-owned and must outlive the calls that record them.
  * Returns PA_ERR_NULL if exactly one argument is NULL.
  */

@@ -336,28 +336,36 @@ template <int DT, int D, int B, int GP>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a) {
   using W = DecodeWave<DT, D, B, GP>;
   extern __shared__ int sm_pre[];   // [S + 1] prefix sums of blocks per sequence
-  __shared__ int sm_scan[kThreads];
+  __shared__ int sm_wsum[kWaves];
   const int S = a.num_seqs, H = a.num_heads, Hk = a.num_kv_heads, G = a.group;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // block counts per sequence and their prefix sums (Hillis-Steele per 256)
+  // Block counts per sequence and their prefix sums, 256 sequences per round:
+  // an inclusive scan inside each wave (shuffles), then the wave totals
+  // through LDS (two barriers per round).
   int carry = 0;
   if (tid == 0) sm_pre[0] = 0;
   for (int base = 0; base < S; base += kThreads) {
     const int s = base + tid;
     const int L = s < S ? min(max(a.context_lens[s], 0), a.max_context_len) : 0;
     int v = (L + B - 1) / B;
-    sm_scan[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const int add = tid >= off ? sm_scan[tid - off] : 0;
-      __syncthreads();
-      v += add;
-      sm_scan[tid] = v;
-      __syncthreads();
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off, 64);
+      v += lane >= off ? t : 0;
     }
-    if (s < S) sm_pre[s + 1] = carry + v;
-    carry += sm_scan[kThreads - 1];
+    if (lane == 63) sm_wsum[wave] = v;
+    __syncthreads();
+    int before = carry;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int t = sm_wsum[w];
+      before += w < wave ? t : 0;
+      carry += t;
+    }
+    if (s < S) sm_pre[s + 1] = before + v;
     __syncthreads();
   }
   const int total = Hk * __builtin_amdgcn_readfirstlane(sm_pre[S]);
@@ -375,8 +383,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
     for (int s = tid; s <= S; s += kThreads) a.plan[2 + s] = sm_pre[s];
   }
 
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wid = blockIdx.x * kWaves + wave;
   int f = wid * chunk;
   const int f_end = min(f + chunk, total);
@@ -701,11 +707,8 @@ static hipError_t launch_decode_t(int num_seqs, const AttnArgs& a, hipStream_t s
                                   const KernelEvents& ev) {
   if (a.plan) {   // balanced split
     const size_t smem = ((size_t)num_seqs + 1) * sizeof(int);
-    if (ev.start) (void)hipEventRecord(ev.start, st);
-    hipLaunchKernelGGL((decode_split_kernel<DT, D, B, GP>), dim3(a.split_workgroups),
-                       dim3(kThreads), smem, st, a);
-    hipError_t e = hipGetLastError();
-    if (ev.stop) (void)hipEventRecord(ev.stop, st);
+    hipError_t e = launch_main(decode_split_kernel<DT, D, B, GP>, dim3(a.split_workgroups),
+                               dim3(kThreads), smem, st, ev, a);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((split_merge_kernel<D>), dim3(a.num_heads, num_seqs), dim3(D), 0, st, a);
     return hipGetLastError();
@@ -713,10 +716,8 @@ static hipError_t launch_decode_t(int num_seqs, const AttnArgs& a, hipStream_t s
   // per-row mode launches one grid row per (sequence, query row) slot
   const int rows = a.q_offsets ? num_seqs * a.max_q_len : num_seqs;
   dim3 grid(a.max_parts, a.num_kv_heads, rows);
-  if (ev.start) (void)hipEventRecord(ev.start, st);
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, B, GP>), grid, dim3(kThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (ev.stop) (void)hipEventRecord(ev.stop, st);
+  hipError_t e = launch_main(decode_partition_kernel<DT, D, B, GP>, grid, dim3(kThreads), 0, st,
+                             ev, a);
   if (e != hipSuccess || a.max_parts <= 1) return e;
   return launch_merge(D, num_seqs, a, st);
 }

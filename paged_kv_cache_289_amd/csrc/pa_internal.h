@@ -3,6 +3,7 @@
 // the hipError_t of the launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -65,6 +66,22 @@ struct KernelEvents {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
+
+// Launch of a call's main kernel.  When profiling events are given they are
+// handed to hipExtLaunchKernel, which stamps them with the dispatch's own start
+// and end (no separate marker packets around it), so they time the kernel as
+// a kernel trace does.
+template <typename K>
+inline hipError_t launch_main(K kernel, dim3 grid, dim3 block, size_t smem, hipStream_t st,
+                              const KernelEvents& ev, const AttnArgs& a) {
+  if (ev.start || ev.stop) {
+    void* args[] = {const_cast<AttnArgs*>(&a)};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, smem, st,
+                              ev.start, ev.stop, 0);
+  }
+  hipLaunchKernelGGL(kernel, grid, block, smem, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(int dtype, int head_dim, int block_size, int group, int num_seqs,
                          const AttnArgs& a, hipStream_t stream, const KernelEvents& ev);

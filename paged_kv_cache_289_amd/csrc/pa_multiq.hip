@@ -481,13 +481,9 @@ static hipError_t launch_mfma_t(int num_seqs, const AttnArgs& a, hipStream_t st,
   const bool rows = multiq_rows_mode(a.max_q_len, a.group);
   const int units = rows ? (rt_count + kWaves - 1) / kWaves : rt_count;
   dim3 grid(units * a.max_parts, a.num_kv_heads, num_seqs);
-  if (ev.start) (void)hipEventRecord(ev.start, st);
-  if (rows)
-    hipLaunchKernelGGL((multiq_mfma_rows_kernel<DT, D, B>), grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((multiq_mfma_kernel<DT, D, B>), grid, dim3(kThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (ev.stop) (void)hipEventRecord(ev.stop, st);
+  const hipError_t e =
+      rows ? launch_main(multiq_mfma_rows_kernel<DT, D, B>, grid, dim3(kThreads), 0, st, ev, a)
+           : launch_main(multiq_mfma_kernel<DT, D, B>, grid, dim3(kThreads), 0, st, ev, a);
   if (e != hipSuccess || a.max_parts <= 1) return e;
   return launch_merge(D, num_seqs, a, st);
 }

@@ -103,6 +103,22 @@ def test_decode_edge_contexts(part):
     U.assert_close(out, want, "bf16", "edges")
 
 
+@pytest.mark.parametrize("num_seqs", [255, 256, 257, 700])
+def test_decode_many_sequences(num_seqs):
+    """Batches that take one, two and three rounds of the in-kernel prefix scan over
+    256 sequences; some contexts are empty, so their blocks count zero."""
+    rng = np.random.default_rng(num_seqs)
+    lens = rng.integers(0, 90, size=num_seqs)
+    lens[::37] = 0
+    st = W.allocate(f"many_{num_seqs}", "bf16", lens, [1] * num_seqs, 8, 2, 64, 16, rng, 9)
+    vals = W.host_values(st)
+    U.say(f"decode {num_seqs} sequences, sum L = {int(lens.sum())}")
+    want = U.oracle_decode(st, vals)
+    for part in (0, 32):
+        out = U.run_decode(st, U.upload(st, vals), out_dtype=torch.float32, partition_tokens=part)
+        U.assert_close(out, want, "bf16", f"{num_seqs} seqs part={part}")
+
+
 def test_decode_all_contexts_empty():
     rng = np.random.default_rng(6)
     st = W.allocate("empty", "bf16", [0, 0], [1, 1], 8, 2, 128, 16, rng, 6)
