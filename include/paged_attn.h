@@ -59,7 +59,9 @@ typedef enum {
   PA_ERR_SHAPE = -2,       /* inconsistent or negative sizes                   */
   PA_ERR_UNSUPPORTED = -3, /* dtype / head_dim / block_size / group not built  */
   PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required       */
-  PA_ERR_HIP = -5          /* a HIP launch or runtime call failed              */
+  PA_ERR_HIP = -5,         /* a HIP launch or runtime call failed              */
+  PA_ERR_NO_BLOCKS = -6,   /* the block pool has too few free blocks           */
+  PA_ERR_INVALID = -7      /* unknown or released sequence id, bad block id    */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -177,6 +179,99 @@ int paged_attn_default_partition(int num_seqs, int num_heads, int num_kv_heads, 
 
 /* Static description of a status code. */
 const char* paged_attn_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Filling and sharing the cache
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Writes the K and V of new tokens into their slots of the pool.  Each decode
+ * step adds the new tokens' K/V to the cache that later steps read ("vLLM:
+ * LLM Inference That Doesn't Waste Your GPU", section "KV cache, in one
+ * picture"), at the slot its position maps to through the block table
+ * ("Local_LLM_03_vLLM_Architecture", PagedAttention slide).
+ *
+ * k_new, v_new: DEVICE [total_new][num_kv_heads][head_dim], dtype.  The new
+ * tokens of sequence s are rows q_offsets[s] .. q_offsets[s+1]-1 (int32
+ * [num_seqs+1], device, non-decreasing, q_offsets[num_seqs] == total_new).
+ * With the attention calls' convention, context_lens[s] already counts them,
+ * so new token i of s goes to position t = context_lens[s] - n_s + i, i.e.
+ * block block_tables[s][t / block_size], slot t % block_size, every KV head.
+ * Bytes are copied unchanged.  Call it before the attention call that reads
+ * the new tokens, on the same stream.  Tokens whose position falls outside
+ * [0, max_context_len) or whose table entry is outside [0, num_blocks) are
+ * skipped (nothing is written out of bounds).  Slots written by two new
+ * tokens at once (tables that alias a block being written) are a caller
+ * error: the pool below never lets a sequence write into a shared block.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (negative sizes, max_context_len beyond
+ * max_blocks_per_seq * block_size, total_new > 0 with num_seqs == 0),
+ * PA_ERR_UNSUPPORTED (dtype, or a row not a multiple of 16 bytes, or
+ * pointers not 16-byte aligned), PA_ERR_HIP.
+ */
+int paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* q_offsets, int num_seqs, int total_new, int num_kv_heads,
+                    int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                    int max_context_len, int dtype, pa_stream_t stream);
+
+/*
+ * Copies whole blocks of both pools: for p < num_pairs, block pairs[2p+1]
+ * receives what block pairs[2p] holds (every KV head and slot of K and of V).
+ * pairs is DEVICE int32 [num_pairs][2]; destinations must be distinct and
+ * never a source.  This is the device half of copy-on-write: run the pairs
+ * that paged_seq_append returns before paged_kv_append writes the new tokens.
+ * Pairs with an id outside [0, num_blocks) are skipped.  Errors as for
+ * paged_kv_append.
+ */
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
+                         int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                         int dtype, pa_stream_t stream);
+
+/*
+ * Host-side block pool: the allocator that hands out the physical blocks the
+ * tables point at.  A sequence of L tokens holds ceil(L / block_size) blocks,
+ * so it wastes fewer than block_size slots ("Scaling inference with vLLM",
+ * paging paragraph; "vLLM: LLM Inference That Doesn't Waste Your GPU",
+ * section "PagedAttention: virtual memory for KV").  A fork shares all of
+ * the parent's blocks instead of copying them ("Scaling inference with vLLM",
+ * prefix-sharing paragraph); every block counts the tables that hold it and
+ * returns to the free list when none does.
+ *
+ * Everything here is HOST memory and host work (no HIP call).  Sequence ids
+ * are small non-negative ints; a released id may be handed out again.  Each
+ * call takes the pool's mutex, so a pool may be shared between threads.
+ *
+ * paged_pool_create returns NULL for num_blocks < 1, block_size < 1 or when
+ * out of host memory.  The int-returning calls return a negative pa_status
+ * on error: PA_ERR_NULL for a NULL pool (or output pointer), PA_ERR_INVALID
+ * for an unknown or released sequence id or a block id outside the pool.
+ *
+ * paged_seq_append grows a sequence by num_tokens (>= 0) and allocates the
+ * blocks they need.  If the sequence's last block is partially filled and
+ * also held by another table, the sequence first gets a fresh copy of it
+ * (copy-on-write): the (source, destination) pair is written to copy_pairs
+ * (host int32, room for max_pairs pairs; at most one pair per call) and
+ * *num_pairs says how many; the caller copies them on the device with
+ * paged_kv_copy_blocks before writing the new tokens.  All or nothing:
+ * PA_ERR_NO_BLOCKS (too few free blocks) and PA_ERR_SHAPE (num_tokens < 0,
+ * or a copy is needed and max_pairs < 1) leave the pool unchanged.
+ *
+ * paged_seq_blocks writes the sequence's block ids, in logical order, to
+ * out (host, room for max_blocks entries) and returns how many; PA_ERR_SHAPE
+ * if max_blocks is too small.  Those ids are the sequence's block-table row.
+ */
+typedef struct paged_block_pool paged_block_pool;
+paged_block_pool* paged_pool_create(int num_blocks, int block_size);
+void paged_pool_destroy(paged_block_pool* pool);
+int paged_pool_num_free(const paged_block_pool* pool);
+int paged_pool_refcount(const paged_block_pool* pool, int block);
+int paged_seq_create(paged_block_pool* pool);
+int paged_seq_fork(paged_block_pool* pool, int parent);
+int paged_seq_release(paged_block_pool* pool, int seq);
+int paged_seq_append(paged_block_pool* pool, int seq, int num_tokens, int32_t* copy_pairs,
+                     int max_pairs, int* num_pairs);
+int paged_seq_length(const paged_block_pool* pool, int seq);
+int paged_seq_blocks(const paged_block_pool* pool, int seq, int32_t* out, int max_blocks);
 
 #ifdef __cplusplus
 }

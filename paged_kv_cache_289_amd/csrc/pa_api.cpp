@@ -154,6 +154,8 @@ const char* paged_attn_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, block_size, group or alignment";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP launch or runtime error";
+    case PA_ERR_NO_BLOCKS: return "block pool has too few free blocks";
+    case PA_ERR_INVALID: return "unknown or released sequence id, or block id outside the pool";
     default: return "unknown status";
   }
 }
@@ -348,6 +350,50 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v
                                     token_offsets, num_seqs, num_kv_heads, head_dim, block_size,
                                     max_blocks_per_seq, max_blocks_per_seq, elem_bytes(dtype),
                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* q_offsets, int num_seqs, int total_new, int num_kv_heads,
+                    int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                    int max_context_len, int dtype, pa_stream_t stream) {
+  if (num_seqs < 0 || total_new < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 ||
+      num_blocks < 1 || max_blocks_per_seq < 1 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+  if (total_new > 0 && num_seqs == 0) return PA_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if ((head_dim * elem_bytes(dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  // one thread per 16-byte chunk: the grid must fit a 32-bit workgroup count
+  const int64_t chunks = (int64_t)total_new * num_kv_heads * (head_dim * elem_bytes(dtype) / 16);
+  if (chunks / 256 >= 0x7fffffff) return PA_ERR_SHAPE;
+  if (total_new == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !block_tables || !context_lens || !q_offsets)
+    return PA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return PA_ERR_UNSUPPORTED;
+  hipError_t e = pa::launch_append(k_cache, v_cache, k_new, v_new, block_tables, context_lens,
+                                   q_offsets, num_seqs, total_new, num_kv_heads, head_dim,
+                                   block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                                   elem_bytes(dtype), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
+                         int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                         int dtype, pa_stream_t stream) {
+  if (num_pairs < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+    return PA_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (((int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype)) % 16 != 0)
+    return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return PA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
+  hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, num_kv_heads,
+                                        head_dim, block_size, num_blocks, elem_bytes(dtype),
+                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -18,6 +18,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedat
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = \
     0, -1, -2, -3, -4, -5
+PA_ERR_NO_BLOCKS, PA_ERR_INVALID = -6, -7
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 
 _TORCH_DT = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
@@ -35,6 +36,18 @@ SIGNATURES = {
     "paged_attn_default_partition": (_I, [_I, _I, _I, _I, _I, _I]),
     "paged_attn_set_kernel_events": (_I, [_P, _P]),
     "paged_attn_status_string": (ctypes.c_char_p, [_I]),
+    "paged_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "paged_kv_copy_blocks": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "paged_pool_create": (_P, [_I, _I]),
+    "paged_pool_destroy": (None, [_P]),
+    "paged_pool_num_free": (_I, [_P]),
+    "paged_pool_refcount": (_I, [_P, _I]),
+    "paged_seq_create": (_I, [_P]),
+    "paged_seq_fork": (_I, [_P, _I]),
+    "paged_seq_release": (_I, [_P, _I]),
+    "paged_seq_append": (_I, [_P, _I, _I, _P, _I, _P]),
+    "paged_seq_length": (_I, [_P, _I]),
+    "paged_seq_blocks": (_I, [_P, _I, _P, _I]),
 }
 
 
@@ -270,3 +283,93 @@ def check_inputs(block_tables: torch.Tensor, context_lens: torch.Tensor, block_s
                                      num_blocks, mbs, max_context_len, _ptr(bad), _stream(stream))
     _check("paged_attn_check_inputs", rc)
     return bad
+
+
+# --------------------------------------------------------------------------
+# filling and sharing the cache
+# --------------------------------------------------------------------------
+
+def append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, q_offsets: torch.Tensor,
+           max_context_len: int, stream=None):
+    """Write new tokens' K/V ``[total_new, Hk, D]`` into their pool slots (in place).
+    New token i of sequence s takes position ``context_lens[s] - n_s + i``."""
+    _need_contig(k_cache=k_cache, v_cache=v_cache, k_new=k_new, v_new=v_new,
+                 block_tables=block_tables, context_lens=context_lens, q_offsets=q_offsets)
+    NB, Hk, B, D = k_cache.shape
+    T = k_new.shape[0]
+    S = context_lens.shape[0]
+    assert k_new.shape == (T, Hk, D) and v_new.shape == k_new.shape
+    assert k_new.dtype == k_cache.dtype and q_offsets.shape[0] == S + 1
+    rc = LIB.paged_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                             _ptr(block_tables), _ptr(context_lens), _ptr(q_offsets), S, T, Hk, D,
+                             B, NB, block_tables.shape[1], int(max_context_len),
+                             _dtype(k_cache), _stream(stream))
+    _check("paged_kv_append", rc)
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor, stream=None):
+    """Block ``pairs[p, 1]`` of both pools receives block ``pairs[p, 0]`` (in place);
+    ``pairs`` is int32 ``[n, 2]`` on the device."""
+    _need_contig(k_cache=k_cache, v_cache=v_cache, pairs=pairs)
+    NB, Hk, B, D = k_cache.shape
+    assert pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2
+    rc = LIB.paged_kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0], Hk,
+                                  D, B, NB, _dtype(k_cache), _stream(stream))
+    _check("paged_kv_copy_blocks", rc)
+
+
+class BlockPool:
+    """The library's host block pool (``paged_pool_*`` / ``paged_seq_*``)."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._h = LIB.paged_pool_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise PagedAttnError("paged_pool_create", PA_ERR_SHAPE, "bad sizes or no memory")
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self):
+        if self._h:
+            LIB.paged_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @staticmethod
+    def _ok(fn: str, rc: int) -> int:
+        if rc < 0:
+            _check(fn, rc)
+        return rc
+
+    def num_free(self) -> int:
+        return self._ok("paged_pool_num_free", LIB.paged_pool_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return self._ok("paged_pool_refcount", LIB.paged_pool_refcount(self._h, int(block)))
+
+    def create(self) -> int:
+        return self._ok("paged_seq_create", LIB.paged_seq_create(self._h))
+
+    def fork(self, parent: int) -> int:
+        return self._ok("paged_seq_fork", LIB.paged_seq_fork(self._h, int(parent)))
+
+    def release(self, seq: int):
+        self._ok("paged_seq_release", LIB.paged_seq_release(self._h, int(seq)))
+
+    def append(self, seq: int, num_tokens: int):
+        """Grow ``seq``; returns the (src, dst) block copies to run on the device first."""
+        pairs = (ctypes.c_int32 * 2)()
+        n = ctypes.c_int(0)
+        self._ok("paged_seq_append", LIB.paged_seq_append(self._h, int(seq), int(num_tokens),
+                                                          pairs, 1, ctypes.byref(n)))
+        return [(pairs[0], pairs[1])] if n.value else []
+
+    def length(self, seq: int) -> int:
+        return self._ok("paged_seq_length", LIB.paged_seq_length(self._h, int(seq)))
+
+    def blocks(self, seq: int):
+        cap = -(-self.length(seq) // self.block_size)
+        buf = (ctypes.c_int32 * max(cap, 1))()
+        n = self._ok("paged_seq_blocks", LIB.paged_seq_blocks(self._h, int(seq), buf, cap))
+        return list(buf[:n])

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert ops.status_string(st)
     assert ops.status_string(-99) == "unknown status"
 
