@@ -36,6 +36,8 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 DECODE = ("llama3_8b_decode", "llama3_70b_decode", "shared_prefix_mix", "tiny_fp32")
 MULTIQ = ("spec_verify", "chunked_prefill")
+APPEND = ("kv_append",)
+APPEND_METRIC = "paged KV append: achieved HBM GB/s (new K/V read + written)"
 
 
 def parse():
@@ -43,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="llama3_8b_decode", choices=DECODE + MULTIQ)
+    ap.add_argument("--workload", default="llama3_8b_decode", choices=DECODE + MULTIQ + APPEND)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--replicas", type=int, default=None,
                     help="K/V pool replicas rotated between steps (default: >= 2 GiB in total)")
@@ -169,6 +171,109 @@ def cpu_baseline(st, dv, budget_s, is_multiq):
 
 
 # ---------------------------------------------------------------------------
+# KV append (prefill chunks written into their slots)
+# ---------------------------------------------------------------------------
+
+def append_bench(a, st):
+    """One step = one paged_kv_append call writing every sequence's new chunk.  The
+    new rows are rotated among replicas so that the Infinity Cache cannot serve
+    a step's reads from the previous one."""
+    import torch
+    import oracle.kv_cache as OK
+    from paged_kv_cache_289_amd import ops, workloads as W
+    dev = torch.device("cuda:0")
+    T, Hk, D, B = st.total_q, st.num_kv_heads, st.head_dim, st.block_size
+    tables = torch.from_numpy(st.block_tables).to(dev)
+    lens = torch.from_numpy(st.context_lens).to(dev)
+    qoff = torch.from_numpy(st.q_offsets).to(dev)
+    dv = W.device_values(st, dev)
+    kc, vc = dv["k_cache"], dv["v_cache"]
+    new_bytes = 2 * T * Hk * D * st.elem_bytes          # K and V rows of the new tokens
+    reps = a.replicas or min(8, max(2, math.ceil(512 * 2**20 / new_bytes)))
+    g = torch.Generator(device=dev)
+    g.manual_seed(a.seed * 7919 + 11)
+    news = [tuple(torch.randn((T, Hk, D), generator=g, device=dev).to(kc.dtype)
+                  for _ in range(2)) for _ in range(reps)]
+    steps = a.steps if a.steps is not None else 100
+    warm = a.warmup if a.warmup is not None else 10
+    stream = torch.cuda.current_stream()
+    fn = ops.LIB.paged_kv_append
+    args = [ctypes.c_void_p(kc.data_ptr()), ctypes.c_void_p(vc.data_ptr()), None, None,
+            ctypes.c_void_p(tables.data_ptr()), ctypes.c_void_p(lens.data_ptr()),
+            ctypes.c_void_p(qoff.data_ptr()), st.num_seqs, T, Hk, D, B, st.num_blocks,
+            st.block_tables.shape[1], st.max_context_len, ops._dtype(kc),
+            ctypes.c_void_p(int(stream.cuda_stream))]
+    ptrs = [(ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr())) for k, v in news]
+
+    def call(i):
+        args[2], args[3] = ptrs[i % reps]
+        rc = fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"paged_kv_append returned {rc}")
+
+    for i in range(warm):
+        call(i)
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in kev:
+        e0.record(stream)
+        e1.record(stream)
+    kev_ptrs = [(ctypes.c_void_p(e0.cuda_event), ctypes.c_void_p(e1.cuda_event)) for e0, e1 in kev]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        ops.LIB.paged_attn_set_kernel_events(*kev_ptrs[i])
+        call(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ops.set_kernel_events(None, None)
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / steps
+    kernel_ms = np.array([e0.elapsed_time(e1) for e0, e1 in kev])
+    algo = 2 * new_bytes                                  # read once, written once
+    value = algo / (ms_per_step * 1e-3) / 1e9
+    kern = float(kernel_ms.mean())
+    ach = algo / (kern * 1e-3) / 1e9
+    res = {
+        "metric": APPEND_METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": st.dtype,
+        "data": "synthetic",
+        "config": {"workload": st.name, "num_seqs": st.num_seqs, "new_tokens": T,
+                   "num_kv_heads": Hk, "head_dim": D, "block_size": B,
+                   "pool_blocks": st.num_blocks, "new_row_replicas": reps, "seed": a.seed},
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "kernel_ms": {"mean": round(kern, 5), "p50": round(float(np.median(kernel_ms)), 5)},
+        "wall_s_timed": round(wall, 3), "source_hash": source_hash(),
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic(st.name, source_hash()),
+                     "kernel": "append kernel", "algorithmic_bytes_per_launch": int(algo)},
+    }
+    if a.cpu_seconds > 0:
+        log("[bench] timing the CPU oracle on the whole workload")
+        host = {k: W.torch_to_host(v, st.dtype) for k, v in
+                (("k", kc), ("v", vc), ("kn", news[0][0]), ("vn", news[0][1]))}
+        c0 = time.perf_counter()
+        OK.append_kv(host["k"], host["v"], host["kn"], host["vn"], st.block_tables,
+                     st.context_lens, st.q_offsets, B)
+        spent = time.perf_counter() - c0
+        res["cpu_baseline"] = {"value": round(algo / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"the whole workload ({T} new tokens) in {spent:.1f} s, "
+                                         f"NumPy, one thread (the oracle copies both pools first)"}
+    else:
+        res["cpu_baseline"] = None
+    line = json.dumps(res)
+    print(line, flush=True)
+    if a.json_out:
+        with open(a.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+# ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
 
@@ -196,6 +301,9 @@ def main():
 
     is_multiq = a.workload in MULTIQ
     st = make_structure(a.workload, a.seed, a.layers)
+    if a.workload in APPEND:
+        log(f"[bench] {st.name}: {json.dumps(st.summary())}")
+        return append_bench(a, st)
     layers = st.layers
     kv_call = kv_bytes_of(st)
     steps = a.steps if a.steps is not None else (10 if layers > 1 else 100)

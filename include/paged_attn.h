@@ -161,7 +161,8 @@ int paged_attn_check_inputs(const int32_t* block_tables, const int32_t* context_
 
 /*
  * Profiling aid.  With both arguments non-NULL (hipEvent_t handles), every
- * later paged_attn_decode / paged_attn_multiq call made from this host thread
+ * later paged_attn_decode / paged_attn_multiq / paged_kv_append call made from
+ * this host thread
  * launches its main kernel with hipExtLaunchKernel, which stamps `start` and
  * `stop` with that dispatch's own start and end on the call's stream (a
  * partition merge, if any, runs after `stop`), so the elapsed time between

@@ -376,7 +376,8 @@ int paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void*
   hipError_t e = pa::launch_append(k_cache, v_cache, k_new, v_new, block_tables, context_lens,
                                    q_offsets, num_seqs, total_new, num_kv_heads, head_dim,
                                    block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                                   elem_bytes(dtype), static_cast<hipStream_t>(stream));
+                                   elem_bytes(dtype), static_cast<hipStream_t>(stream),
+                                   t_events);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -52,15 +52,25 @@ hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const 
                          const int32_t* block_tables, const int32_t* context_lens,
                          const int32_t* q_offsets, int num_seqs, int total_new, int num_kv_heads,
                          int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
-                         int max_context_len, int elem_bytes, hipStream_t st) {
-  const int cpr = head_dim * elem_bytes / 16;
+                         int max_context_len, int elem_bytes, hipStream_t st,
+                         const KernelEvents& ev) {
+  int cpr = head_dim * elem_bytes / 16;
   const int64_t threads = (int64_t)total_new * num_kv_heads * cpr;
-  const int64_t wgs = (threads + 255) / 256;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)wgs), dim3(256), 0, st,
-                     reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache),
-                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
-                     block_tables, context_lens, q_offsets, num_seqs, total_new, num_kv_heads,
-                     cpr, block_size, num_blocks, max_blocks_per_seq, max_context_len);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  uint4* kc = reinterpret_cast<uint4*>(k_cache);
+  uint4* vc = reinterpret_cast<uint4*>(v_cache);
+  const uint4* kn = reinterpret_cast<const uint4*>(k_new);
+  const uint4* vn = reinterpret_cast<const uint4*>(v_new);
+  if (ev.start || ev.stop) {   // profiling: events stamped by the dispatch itself
+    void* args[] = {&kc, &vc, &kn, &vn, &block_tables, &context_lens, &q_offsets, &num_seqs,
+                    &total_new, &num_kv_heads, &cpr, &block_size, &num_blocks,
+                    &max_blocks_per_seq, &max_context_len};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(append_kernel), grid, dim3(256), args,
+                              0, st, ev.start, ev.stop, 0);
+  }
+  hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, st, kc, vc, kn, vn, block_tables,
+                     context_lens, q_offsets, num_seqs, total_new, num_kv_heads, cpr, block_size,
+                     num_blocks, max_blocks_per_seq, max_context_len);
   return hipGetLastError();
 }
 

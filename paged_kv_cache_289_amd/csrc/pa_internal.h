@@ -102,7 +102,8 @@ hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const 
                          const int32_t* block_tables, const int32_t* context_lens,
                          const int32_t* q_offsets, int num_seqs, int total_new, int num_kv_heads,
                          int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
-                         int max_context_len, int elem_bytes, hipStream_t stream);
+                         int max_context_len, int elem_bytes, hipStream_t stream,
+                         const KernelEvents& ev);
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
                               int num_kv_heads, int head_dim, int block_size, int num_blocks,

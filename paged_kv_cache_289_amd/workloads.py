@@ -267,6 +267,17 @@ def random_small(seed: int, *, num_seqs: int, num_heads: int, num_kv_heads: int,
                     shared_prefix_blocks=shared_prefix_blocks)
 
 
+def kv_append_chunk(seed: int = 0, num_seqs: int = 64, chunk: int = 512, ctx_lo: int = 512,
+                    ctx_hi: int = 4096, dtype: str = "bf16") -> PagedStructure:
+    """Appending a ``chunk``-token prefill chunk to each of ``num_seqs`` sequences of the
+    Llama-3-8B-like layout (8 KV heads, head_dim 128, 16-token blocks): contexts
+    uniform in [ctx_lo, ctx_hi] count the chunk, whose tokens are the last ones."""
+    srng, _ = _rngs(seed)
+    L = srng.integers(ctx_lo, ctx_hi + 1, size=num_seqs)
+    return allocate(f"kv_append_chunk{chunk}_b{num_seqs}", dtype, L, np.full_like(L, chunk), 32,
+                    8, 128, 16, srng, seed, max_blocks_per_seq=-(-ctx_hi // 16))
+
+
 NAMED = {
     "tiny_fp32": tiny_fp32,
     "llama3_8b_decode": llama3_8b_decode,
@@ -274,6 +285,7 @@ NAMED = {
     "shared_prefix_mix": shared_prefix_mix,
     "spec_verify": spec_verify,
     "chunked_prefill": chunked_prefill,
+    "kv_append": kv_append_chunk,
 }
 
 

@@ -144,3 +144,38 @@ def test_serving_loop_with_forks_and_copy_on_write():
     assert pool.blocks(d)[:2] == pool.blocks(a)[:2]
     assert pool.blocks(d)[2] != pool.blocks(a)[2]
     pool.close()
+
+
+def test_full_size_append():
+    """The benchmark's workload (a 512-token chunk for each of 64 sequences, device
+    values): for sampled sequences the gather after the append is the gather before
+    it over L - n tokens followed by the new rows, bit for bit."""
+    ops = U.ops()
+    st = W.kv_append_chunk(0)
+    U.say(f"full size {st.name}: {st.summary()}")
+    dv = W.device_values(st, U.DEV)
+    kc, vc = dv["k_cache"], dv["v_cache"]
+    g = torch.Generator(device=U.DEV)
+    g.manual_seed(5)
+    kn = torch.randn((st.total_q, st.num_kv_heads, st.head_dim), generator=g,
+                     device=U.DEV).to(kc.dtype)
+    vn = torch.randn_like(kn)
+    t = U.upload(st, {})
+    seqs = sorted({0, int(np.argmax(st.context_lens)), int(np.argmin(st.context_lens)), 41})
+    L = st.context_lens.astype(np.int64)
+    old_lens = torch.from_numpy((L - st.q_lens).astype(np.int32)).to(U.DEV)
+    off_old = np.concatenate([[0], np.cumsum(L - st.q_lens)]).astype(np.int32)
+    off_new = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    bk, bv = ops.gather(kc, vc, t["block_tables"], old_lens, torch.from_numpy(off_old).to(U.DEV),
+                        int(off_old[-1]))
+    ops.append(kc, vc, kn, vn, t["block_tables"], t["context_lens"], t["q_offsets"],
+               st.max_context_len)
+    ak, av = ops.gather(kc, vc, t["block_tables"], t["context_lens"],
+                        torch.from_numpy(off_new).to(U.DEV), int(off_new[-1]))
+    torch.cuda.synchronize()
+    qo = st.q_offsets
+    for s in seqs:
+        for before, new, after in ((bk, kn, ak), (bv, vn, av)):
+            want = torch.cat([before[off_old[s]:off_old[s + 1]], new[qo[s]:qo[s + 1]]])
+            got = after[off_new[s]:off_new[s + 1]]
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"seq {s}"
