@@ -274,6 +274,32 @@ int paged_seq_append(paged_block_pool* pool, int seq, int num_tokens, int32_t* c
 int paged_seq_length(const paged_block_pool* pool, int seq);
 int paged_seq_blocks(const paged_block_pool* pool, int seq, int32_t* out, int max_blocks);
 
+/*
+ * Prefix caching on the pool.  The pages' server hashes each page's token
+ * content, so that requests with the same first N tokens share N / block_size
+ * physical pages and skip recomputing them ("Local_LLM_03_vLLM_Architecture",
+ * prefix-caching slide; "vLLM: LLM Inference That Doesn't Waste Your GPU",
+ * section "Prefix caching").
+ *
+ * paged_seq_commit registers the full blocks among the sequence's first
+ * num_tokens tokens (host int32 token ids, the sequence's own tokens from its
+ * start; num_tokens <= its length; call it once their K/V are written).  A
+ * token prefix that is already registered keeps its block.  Returns how many
+ * blocks were newly registered.
+ *
+ * paged_seq_match_prefix gives an EMPTY sequence (length 0, else
+ * PA_ERR_INVALID) every leading full block registered under exactly the same
+ * token prefix as tokens[0 .. num_tokens): the blocks join its table (their
+ * reference counts go up) and its length becomes the returned number of
+ * tokens, a multiple of block_size.  Their K/V are already in the pool; the
+ * caller appends and computes only the rest.  Hits are verified against the
+ * stored tokens and parent block, so a hash collision never shares a block.
+ * A block leaves the cache when it returns to the free list.
+ */
+int paged_seq_commit(paged_block_pool* pool, int seq, const int32_t* tokens, int num_tokens);
+int paged_seq_match_prefix(paged_block_pool* pool, int seq, const int32_t* tokens,
+                           int num_tokens);
+
 #ifdef __cplusplus
 }
 #endif

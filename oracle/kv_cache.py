@@ -28,6 +28,16 @@ What is computed
   (copy-on-write), while a full shared block is never written again.  Which
   free block is handed out is the allocator's choice; the model picks the
   lowest id, and tests compare only what does not depend on that choice.
+* **Prefix caching.**  The pages' server hashes each page's token content, and
+  two requests with the same first ``N`` tokens share ``N / B`` physical pages
+  with no recomputation ("Local_LLM_03_vLLM_Architecture", prefix-caching
+  slide; "vLLM: LLM Inference That Doesn't Waste Your GPU", section "Prefix
+  caching").  The model keys a full block by the exact tokens from the start
+  of the sequence to the end of that block (the plain meaning of "the same
+  first N tokens"): ``commit`` registers a sequence's full blocks once their
+  K/V are written, ``match_prefix`` gives an empty sequence every leading
+  full block already registered under the same token prefix.  A block leaves
+  the cache when it returns to the free set.
 """
 from __future__ import annotations
 
@@ -85,6 +95,7 @@ class BlockPoolModel:
         self.blocks: Dict[int, List[int]] = {}
         self.length: Dict[int, int] = {}
         self._next_seq = 0
+        self.cached: Dict[tuple, int] = {}      # token prefix through a full block -> block
 
     def _take(self) -> int:
         b = min(self.free)
@@ -97,6 +108,7 @@ class BlockPoolModel:
         if self.ref[b] == 0:
             del self.ref[b]
             self.free.add(b)
+            self.cached = {k: v for k, v in self.cached.items() if v != b}
 
     def create(self) -> int:
         s = self._next_seq
@@ -139,6 +151,34 @@ class BlockPoolModel:
             self.blocks[s].append(self._take())
         self.length[s] = L + n
         return pairs
+
+    def match_prefix(self, s: int, tokens: Sequence[int]) -> int:
+        """Point the empty sequence ``s`` at every leading full block registered
+        under the same token prefix; returns the number of tokens it now holds."""
+        assert self.length[s] == 0
+        B, j = self.B, 0
+        while (j + 1) * B <= len(tokens):
+            b = self.cached.get(tuple(tokens[:(j + 1) * B]))
+            if b is None:
+                break
+            self.blocks[s].append(b)
+            self.ref[b] += 1
+            j += 1
+        self.length[s] = j * B
+        return j * B
+
+    def commit(self, s: int, tokens: Sequence[int]) -> int:
+        """Register the full blocks of ``s`` among its first ``len(tokens)`` tokens
+        (whose K/V are written); a prefix already registered keeps its block.
+        Returns how many blocks were newly registered."""
+        assert len(tokens) <= self.length[s]
+        new = 0
+        for j in range(len(tokens) // self.B):
+            key = tuple(tokens[:(j + 1) * self.B])
+            if key not in self.cached:
+                self.cached[key] = self.blocks[s][j]
+                new += 1
+        return new
 
     def num_free(self) -> int:
         return len(self.free)

@@ -48,6 +48,8 @@ SIGNATURES = {
     "paged_seq_append": (_I, [_P, _I, _I, _P, _I, _P]),
     "paged_seq_length": (_I, [_P, _I]),
     "paged_seq_blocks": (_I, [_P, _I, _P, _I]),
+    "paged_seq_commit": (_I, [_P, _I, _P, _I]),
+    "paged_seq_match_prefix": (_I, [_P, _I, _P, _I]),
 }
 
 
@@ -373,3 +375,16 @@ class BlockPool:
         buf = (ctypes.c_int32 * max(cap, 1))()
         n = self._ok("paged_seq_blocks", LIB.paged_seq_blocks(self._h, int(seq), buf, cap))
         return list(buf[:n])
+
+    def commit(self, seq: int, tokens) -> int:
+        """Register the full blocks of ``seq``'s first ``len(tokens)`` tokens (K/V written)."""
+        buf = (ctypes.c_int32 * max(len(tokens), 1))(*tokens)
+        return self._ok("paged_seq_commit", LIB.paged_seq_commit(self._h, int(seq), buf,
+                                                                 len(tokens)))
+
+    def match_prefix(self, seq: int, tokens) -> int:
+        """Give the empty ``seq`` the cached blocks of its leading tokens; returns how many
+        tokens it now holds."""
+        buf = (ctypes.c_int32 * max(len(tokens), 1))(*tokens)
+        return self._ok("paged_seq_match_prefix",
+                        LIB.paged_seq_match_prefix(self._h, int(seq), buf, len(tokens)))

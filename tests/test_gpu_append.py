@@ -179,3 +179,64 @@ def test_full_size_append():
             want = torch.cat([before[off_old[s]:off_old[s + 1]], new[qo[s]:qo[s + 1]]])
             got = after[off_new[s]:off_new[s + 1]]
             assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"seq {s}"
+
+
+def test_prefix_cached_prefill():
+    """Request B shares request A's first 35 tokens: it takes A's two full blocks
+    from the prefix cache and writes K/V only for its remaining 18 tokens.  B's
+    cache is then A's first 32 K/V rows followed by its own, bit for bit, and
+    decoding both matches the fp64 oracle over those histories."""
+    ops = U.ops()
+    dtype, NB, B, Hk, H, D = "bf16", 32, 16, 2, 4, 64
+    scale = 1.0 / np.sqrt(D)
+    rng = np.random.default_rng(77)
+    pool = ops.BlockPool(NB, B)
+    kc = torch.zeros((NB, Hk, B, D), dtype=torch.bfloat16, device=U.DEV)
+    vc = torch.zeros_like(kc)
+    tok_a = [int(x) for x in rng.integers(0, 32000, 40)]
+    tok_b = tok_a[:35] + [int(x) for x in rng.integers(0, 32000, 15)]
+
+    def write(seq, rows_k, rows_v):
+        L, n = pool.length(seq), rows_k.shape[0]
+        blocks = pool.blocks(seq)
+        dt = W.host_to_torch({"k": rows_k, "v": rows_v, "tbl": np.array([blocks], np.int32),
+                              "lens": np.array([L], np.int32),
+                              "qoff": np.array([0, n], np.int32)}, dtype, U.DEV)
+        ops.append(kc, vc, dt["k"], dt["v"], dt["tbl"], dt["lens"], dt["qoff"], len(blocks) * B)
+
+    a = pool.create()
+    assert pool.match_prefix(a, tok_a) == 0
+    pool.append(a, 40)
+    ka, va = (_new_rows(rng, 40, Hk, D, dtype) for _ in range(2))
+    write(a, ka, va)
+    assert pool.commit(a, tok_a) == 2
+    b = pool.create()
+    assert pool.match_prefix(b, tok_b) == 32
+    assert pool.blocks(b)[:2] == pool.blocks(a)[:2]
+    pool.append(b, len(tok_b) - 32)
+    kb, vb = (_new_rows(rng, 18, Hk, D, dtype) for _ in range(2))
+    write(b, kb, vb)
+    hist = {a: (ka, va), b: (np.concatenate([ka[:32], kb]), np.concatenate([va[:32], vb]))}
+
+    seqs = [a, b]
+    lens = np.array([pool.length(s) for s in seqs], np.int32)
+    mbs = int(-(-lens.max() // B))
+    tables = np.zeros((2, mbs), np.int32)
+    for i, s in enumerate(seqs):
+        tables[i, :len(pool.blocks(s))] = pool.blocks(s)
+    toff = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    dt = W.host_to_torch({"tbl": tables, "lens": lens, "toff": toff}, dtype, U.DEV)
+    gk, gv = ops.gather(kc, vc, dt["tbl"], dt["lens"], dt["toff"], int(toff[-1]))
+    gk, gv = W.torch_to_host(gk, dtype), W.torch_to_host(gv, dtype)
+    for i, s in enumerate(seqs):
+        assert np.array_equal(gk[toff[i]:toff[i + 1]], hist[s][0])
+        assert np.array_equal(gv[toff[i]:toff[i + 1]], hist[s][1])
+    q = W.f32_to_bf16_bits(rng.standard_normal((2, H, D)).astype(np.float32))
+    qt = W.host_to_torch({"q": q}, dtype, U.DEV)["q"]
+    out = ops.decode(qt, kc, vc, dt["tbl"], dt["lens"], scale, mbs * B, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = np.stack([OP.attend_rows(OP.widen(q[i:i + 1], dtype), OP.widen(hist[s][0], dtype),
+                                    OP.widen(hist[s][1], dtype), scale, [int(lens[i])])[0]
+                     for i, s in enumerate(seqs)])
+    U.assert_close(out, want, dtype, "prefix-cached decode")
+    pool.close()

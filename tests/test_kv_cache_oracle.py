@@ -240,3 +240,87 @@ def test_pool_mutants_are_caught(cls):
         except (AssertionError, KeyError, ValueError):
             caught += 1
     assert caught > 0
+
+
+# --------------------------------------------------------------------------
+# prefix caching
+# --------------------------------------------------------------------------
+
+def _serve(m, tokens):
+    """A request: take the cached prefix, allocate the rest, register its blocks."""
+    s = m.create()
+    got = m.match_prefix(s, tokens)
+    m.append(s, len(tokens) - got)
+    m.commit(s, tokens)
+    return s, got
+
+
+@pytest.mark.parametrize("N", [0, 7, 16, 40, 48])
+def test_same_first_tokens_share_their_whole_blocks(N):
+    """Two requests with the same first N tokens (then different ones) share
+    N // B physical blocks, and the second computes only the rest."""
+    B = 16
+    m = OK.BlockPoolModel(64, B)
+    rng = random.Random(N)
+    common = [rng.randrange(1000) for _ in range(N)]
+    a, _ = _serve(m, common + [1001] * 30)
+    b, got = _serve(m, common + [1002] * 21)
+    assert got == (N // B) * B
+    assert sum(x == y for x, y in zip(m.table(a), m.table(b))) == N // B
+    assert not model_violations(m, 64)
+
+
+def test_prefix_match_needs_the_whole_prefix():
+    """A block is shared only when everything before it matches too."""
+    B = 4
+    m = OK.BlockPoolModel(32, B)
+    _serve(m, [1, 2, 3, 4, 5, 6, 7, 8])
+    _, got = _serve(m, [9, 2, 3, 4, 5, 6, 7, 8])      # same second block, other first
+    assert got == 0
+    _, got = _serve(m, [1, 2, 3, 4, 5, 6, 7, 8, 9])
+    assert got == 8
+
+
+def test_freed_blocks_leave_the_cache():
+    B = 4
+    m = OK.BlockPoolModel(16, B)
+    a, _ = _serve(m, list(range(12)))
+    m.release(a)
+    assert not m.cached and m.num_free() == 16
+    _, got = _serve(m, list(range(12)))
+    assert got == 0
+
+
+class _ContentOnlyCache(OK.BlockPoolModel):
+    """Planted mistake: blocks keyed by their own tokens, not by the whole prefix."""
+
+    def match_prefix(self, s, tokens):
+        B, j = self.B, 0
+        while (j + 1) * B <= len(tokens):
+            b = self.cached.get(tuple(tokens[j * B:(j + 1) * B]))
+            if b is None:
+                break
+            self.blocks[s].append(b)
+            self.ref[b] += 1
+            j += 1
+        self.length[s] = j * B
+        return j * B
+
+    def commit(self, s, tokens):
+        for j in range(len(tokens) // self.B):
+            self.cached.setdefault(tuple(tokens[j * self.B:(j + 1) * self.B]), self.blocks[s][j])
+        return 0
+
+
+def _pin_first_block_is_not_a_later_block(cls):
+    """A request whose first block equals another request's second block shares
+    nothing with it (the other block's prefix is longer)."""
+    m = cls(32, 4)
+    _serve(m, [1, 2, 3, 4, 5, 6, 7, 8])
+    _, got = _serve(m, [5, 6, 7, 8, 5, 6, 7, 8])
+    return got
+
+
+def test_prefix_cache_mutant_is_caught():
+    assert _pin_first_block_is_not_a_later_block(OK.BlockPoolModel) == 0
+    assert _pin_first_block_is_not_a_later_block(_ContentOnlyCache) != 0

@@ -154,3 +154,52 @@ def test_append_rejects_bad_arguments(kw, code):
 ])
 def test_copy_blocks_rejects_bad_arguments(args, code):
     assert ops.LIB.paged_kv_copy_blocks(*args, None) == code
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefix_cache_matches_model(seed):
+    """Requests built from a few shared templates: the pool shares exactly the
+    blocks the model shares, and matches exactly as many tokens."""
+    NB, B = 96, 4
+    rng = random.Random(seed)
+    templates = [[rng.randrange(50) for _ in range(rng.randint(0, 14))] for _ in range(3)]
+    pool, model = ops.BlockPool(NB, B), OK.BlockPoolModel(NB, B)
+    ids, toks = {}, {}
+    for _ in range(60):
+        if ids and rng.random() < 0.3:
+            s = rng.choice(list(ids))
+            model.release(s)
+            pool.release(ids.pop(s))
+            continue
+        tokens = rng.choice(templates) + [rng.randrange(50) for _ in range(rng.randint(0, 9))]
+        ms, ps = model.create(), pool.create()
+        got_m = model.match_prefix(ms, tokens)
+        got_p = pool.match_prefix(ps, tokens)
+        assert got_p == got_m
+        try:
+            model.append(ms, len(tokens) - got_m)
+        except OK.OutOfBlocks:
+            with pytest.raises(ops.PagedAttnError):
+                pool.append(ps, len(tokens) - got_p)
+            model.release(ms)
+            pool.release(ps)
+            continue
+        pool.append(ps, len(tokens) - got_p)
+        assert pool.commit(ps, tokens) == model.commit(ms, tokens)
+        ids[ms], toks[ms] = ps, tokens
+        _compare(pool, model, ids, NB)
+    pool.close()
+
+
+def test_prefix_cache_errors():
+    pool = ops.BlockPool(8, 4)
+    s = pool.create()
+    pool.append(s, 3)
+    with pytest.raises(ops.PagedAttnError) as e:       # only an empty sequence matches
+        pool.match_prefix(s, [1, 2, 3, 4])
+    assert e.value.status == ops.PA_ERR_INVALID
+    with pytest.raises(ops.PagedAttnError) as e:       # cannot commit past the length
+        pool.commit(s, [1, 2, 3, 4])
+    assert e.value.status == ops.PA_ERR_SHAPE
+    assert pool.commit(s, [1, 2, 3]) == 0              # no full block yet
+    pool.close()
