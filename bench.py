@@ -51,6 +51,9 @@ def parse():
                     help="K/V pool replicas rotated between steps (default: >= 2 GiB in total)")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library's)")
     ap.add_argument("--layers", type=int, default=None, help="override layer count (70B workload)")
+    ap.add_argument("--cascade", action="store_true",
+                    help="shared_prefix_mix: attend the shared prefix once for all sequences "
+                         "(paged_attn_decode_shared_prefix) instead of per sequence")
     ap.add_argument("--block-size", type=int, default=None,
                     help="tokens per block for the Llama-3-8B decode workload (default 16)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -356,6 +359,20 @@ def main():
                                       st.max_context_len, st.max_q_len, out,
                                       partition_tokens=part, workspace=ws, stream=stream)
     else:
+        prepared = None
+    if a.cascade:
+        if a.workload != "shared_prefix_mix":
+            raise SystemExit("--cascade applies to the shared_prefix_mix workload only")
+        # leading table columns that every sequence shares (host-side structure)
+        nb = -(-st.context_lens.astype(np.int64) // st.block_size)
+        P = 0
+        while P < nb.min() and np.all(st.block_tables[:, P] == st.block_tables[0, P]):
+            P += 1
+        prepared = ops.prepare_decode_shared_prefix(q, pools[0][0], pools[0][1], tables, lens,
+                                                    st.scale, st.max_context_len, P, out,
+                                                    stream=stream)
+        part_used = f"shared-prefix cascade over {P} blocks"
+    elif not is_multiq:
         prepared = ops.prepare_decode(q, pools[0][0], pools[0][1], tables, lens, st.scale,
                                       st.max_context_len, out, partition_tokens=part,
                                       workspace=ws, stream=stream)
@@ -386,13 +403,14 @@ def main():
     for step in range(steps):
         for c in range(calls_per_step):
             kc, vc = pools[(step * calls_per_step + c) % npools] if layers == 1 else pools[c]
-            set_events(*kev_ptrs[k])
+            if not a.cascade:   # (the cascade's kernels take no events: whole calls are timed)
+                set_events(*kev_ptrs[k])
             call(kc, vc)
             k += 1
     t_end.record(stream)
     torch.cuda.synchronize()
     ops.set_kernel_events(None, None)
-    kernel_ms = np.array([s.elapsed_time(e) for s, e in kev])
+    kernel_ms = None if a.cascade else np.array([s.elapsed_time(e) for s, e in kev])
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     for k, (e0, e1) in enumerate(ev):     # informational: one call between two events
@@ -436,7 +454,10 @@ def main():
         res["unique_GBps"] = round(ub / (ms_per_step * 1e-3) / 1e9, 2)
 
     # roofline of the dominant kernel (the call's main kernel, bracketed by HIP events that
-    # the library records on the launch stream)
+    # the library records on the launch stream); for the shared-prefix cascade, whose
+    # several kernels share the work, the whole call
+    if kernel_ms is None:
+        kernel_ms = per_call_ms
     kern_ms = float(kernel_ms.mean())
     res["kernel_ms"] = {"mean": round(kern_ms, 5), "p50": round(float(np.median(kernel_ms)), 5)}
     if is_multiq and a.workload == "chunked_prefill":
@@ -451,7 +472,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBPS, 4)}
     roof["traffic"] = measured_traffic(st.name, res["source_hash"])
-    roof["kernel"] = "multi-query main kernel" if is_multiq else "decode split kernel"
+    roof["kernel"] = ("shared-prefix cascade, whole call (prep, prefix multi-query + merge, "
+                      "tail decode + merge, combine)" if a.cascade else
+                      "multi-query main kernel" if is_multiq else "decode split kernel")
     roof["algorithmic_bytes_per_launch"] = int(basis) if basis is not None else None
     if is_multiq:
         res["tflops"] = round(flops_of(st) / (call_ms * 1e-3) / 1e12, 2)

@@ -178,6 +178,39 @@ int paged_attn_set_kernel_events(void* start, void* stop);
 int paged_attn_default_partition(int num_seqs, int num_heads, int num_kv_heads, int block_size,
                                  int max_context_len, int max_q_len);
 
+/*
+ * Decode over a shared prefix.  Same result as paged_attn_decode (same
+ * arguments and conventions), for calls whose block tables all start with the
+ * same prefix_blocks physical blocks -- requests with a common start that
+ * share its pages ("Scaling inference with vLLM", prefix-sharing paragraph;
+ * "Local_LLM_03_vLLM_Architecture", prefix-caching slide) -- and whose
+ * context_lens are all at least prefix_blocks * block_size.  Those are
+ * preconditions, not checked on the device; outside them the result is
+ * undefined.
+ *
+ * The prefix is attended once for all sequences: one multi-query pass treats
+ * the num_seqs decode queries as num_seqs rows over the shared keys (matrix
+ * cores, each prefix K/V tile read once per group of rows), a decode pass
+ * covers each sequence's own tail (its table from entry prefix_blocks on),
+ * and a last kernel combines the two normalized parts by their log-sum-exps.
+ * prefix_blocks == 0 is a plain decode.
+ *
+ * workspace: device, at least paged_attn_shared_prefix_workspace_size(...)
+ * bytes, 16-byte aligned, no initialization needed.  Errors as for
+ * paged_attn_decode, plus PA_ERR_SHAPE for prefix_blocks < 0, beyond
+ * max_blocks_per_seq, or covering more than max_context_len tokens.
+ */
+size_t paged_attn_shared_prefix_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                               int head_dim, int block_size, int max_context_len,
+                                               int prefix_blocks);
+int paged_attn_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, int num_seqs, int num_heads,
+                                    int num_kv_heads, int head_dim, int block_size,
+                                    int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                    int prefix_blocks, float scale, int dtype, int out_dtype,
+                                    void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
 /* Static description of a status code. */
 const char* paged_attn_status_string(int status);
 

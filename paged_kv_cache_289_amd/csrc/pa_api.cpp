@@ -205,12 +205,18 @@ size_t paged_attn_workspace_size(int num_seqs, int total_q, int max_q_len, int n
   return workspace_bytes_for(total_q, num_heads, head_dim, max_parts);
 }
 
-int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
-                      int num_heads, int num_kv_heads, int head_dim, int block_size,
-                      int num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
-                      int dtype, int out_dtype, int partition_tokens, void* workspace,
-                      size_t workspace_bytes, pa_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// paged_attn_decode with an optional per-(row, head) log-sum-exp output (log2
+// units) and the profiling events to use.
+int decode_core(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                int max_blocks_per_seq, int max_context_len, float scale, int dtype, int out_dtype,
+                int partition_tokens, void* workspace, size_t workspace_bytes, pa_stream_t stream,
+                float* lse, const pa::KernelEvents& ev) {
   int rc = check_attn_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                              max_blocks_per_seq, max_context_len, dtype, out_dtype,
                              partition_tokens, scale);
@@ -238,6 +244,7 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
   a.causal = 0;
   a.out_dtype = out_dtype;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.lse = lse;
 
   if (num_seqs <= pa::kMaxSplitSeqs) {
     // the workspace is checked against the device-independent bound (what
@@ -271,17 +278,38 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
     a.plan = nullptr;
   }
   hipError_t e = pa::launch_decode(dtype, head_dim, block_size, a.group, num_seqs, a,
-                                   static_cast<hipStream_t>(stream), t_events);
+                                   static_cast<hipStream_t>(stream), ev);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-int paged_attn_multiq(void* out, const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_tables, const int32_t* context_lens,
-                      const int32_t* q_offsets, int num_seqs, int total_q, int max_q_len,
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                       int num_heads, int num_kv_heads, int head_dim, int block_size,
                       int num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
-                      int causal, int dtype, int out_dtype, int partition_tokens,
-                      void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+                      int dtype, int out_dtype, int partition_tokens, void* workspace,
+                      size_t workspace_bytes, pa_stream_t stream) {
+  return decode_core(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                     max_context_len, scale, dtype, out_dtype, partition_tokens, workspace,
+                     workspace_bytes, stream, nullptr, t_events);
+}
+
+}  // extern "C"
+
+namespace {
+
+// paged_attn_multiq with an optional log-sum-exp output and the events to use.
+int multiq_core(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens,
+                const int32_t* q_offsets, int num_seqs, int total_q, int max_q_len,
+                int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                int max_blocks_per_seq, int max_context_len, float scale, int causal, int dtype,
+                int out_dtype, int partition_tokens, void* workspace, size_t workspace_bytes,
+                pa_stream_t stream, float* lse, const pa::KernelEvents& ev) {
   int rc = check_attn_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                              max_blocks_per_seq, max_context_len, dtype, out_dtype,
                              partition_tokens, scale);
@@ -324,10 +352,29 @@ int paged_attn_multiq(void* out, const void* q, const void* k_cache, const void*
   a.causal = causal ? 1 : 0;
   a.out_dtype = out_dtype;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.lse = lse;
   hipError_t e = pa::launch_multiq(dtype, head_dim, block_size, a.group, num_seqs, a,
-                                   static_cast<hipStream_t>(stream), t_events);
+                                   static_cast<hipStream_t>(stream), ev);
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_multiq(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* q_offsets, int num_seqs, int total_q, int max_q_len,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
+                      int causal, int dtype, int out_dtype, int partition_tokens,
+                      void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  return multiq_core(out, q, k_cache, v_cache, block_tables, context_lens, q_offsets, num_seqs,
+                     total_q, max_q_len, num_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_blocks_per_seq, max_context_len, scale, causal, dtype,
+                     out_dtype, partition_tokens, workspace, workspace_bytes, stream, nullptr,
+                     t_events);
 }
 
 int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
@@ -350,6 +397,115 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v
                                     token_offsets, num_seqs, num_kv_heads, head_dim, block_size,
                                     max_blocks_per_seq, max_blocks_per_seq, elem_bytes(dtype),
                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of the shared-prefix decode: int32 {q_offsets[2], prefix_len[1],
+// tail_lens[S]}, fp32 outputs and log-sum-exps of both parts, then the
+// workspaces of the prefix multi-query call and of the tail decode, each
+// starting on a 256-byte boundary.
+struct CascadeLayout {
+  size_t ints = 0, out1 = 0, out2 = 0, lse1 = 0, lse2 = 0, mq = 0, dec = 0, total = 0;
+  size_t mq_bytes = 0, dec_bytes = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+CascadeLayout cascade_layout(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_context_len, int prefix_blocks) {
+  CascadeLayout c;
+  const size_t S = (size_t)num_seqs, rows = S * num_heads;
+  const int prefix_tokens = prefix_blocks * block_size;
+  size_t off = 0;
+  c.ints = off;  off = align256(off + (3 + S) * sizeof(int32_t));
+  c.out1 = off;  off = align256(off + rows * head_dim * sizeof(float));
+  c.out2 = off;  off = align256(off + rows * head_dim * sizeof(float));
+  c.lse1 = off;  off = align256(off + rows * sizeof(float));
+  c.lse2 = off;  off = align256(off + rows * sizeof(float));
+  c.mq_bytes = paged_attn_workspace_size(1, num_seqs, num_seqs, num_heads, num_kv_heads,
+                                         head_dim, block_size, prefix_tokens, 0);
+  c.mq = off;    off = align256(off + c.mq_bytes);
+  c.dec_bytes = paged_attn_workspace_size(num_seqs, num_seqs, 1, num_heads, num_kv_heads,
+                                          head_dim, block_size, max_context_len - prefix_tokens, 0);
+  c.dec = off;   off = align256(off + c.dec_bytes);
+  c.total = off;
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attn_shared_prefix_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                               int head_dim, int block_size, int max_context_len,
+                                               int prefix_blocks) {
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 ||
+      max_context_len < 0 || prefix_blocks < 0 || num_heads % num_kv_heads)
+    return 0;
+  if ((int64_t)prefix_blocks * block_size > max_context_len) return 0;
+  if (num_seqs == 0) return 0;
+  if (prefix_blocks == 0)
+    return paged_attn_workspace_size(num_seqs, num_seqs, 1, num_heads, num_kv_heads, head_dim,
+                                     block_size, max_context_len, 0);
+  return cascade_layout(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_context_len, prefix_blocks).total;
+}
+
+int paged_attn_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, int num_seqs, int num_heads,
+                                    int num_kv_heads, int head_dim, int block_size,
+                                    int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                    int prefix_blocks, float scale, int dtype, int out_dtype,
+                                    void* workspace, size_t workspace_bytes,
+                                    pa_stream_t stream) {
+  int rc = check_attn_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             max_blocks_per_seq, max_context_len, dtype, out_dtype, 0, scale);
+  if (rc != PA_OK) return rc;
+  if (prefix_blocks < 0 || prefix_blocks > max_blocks_per_seq ||
+      (int64_t)prefix_blocks * block_size > max_context_len)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  const pa::KernelEvents none{};
+  if (prefix_blocks == 0)
+    return decode_core(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len, scale, dtype, out_dtype, 0, workspace, workspace_bytes,
+                       stream, nullptr, none);
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
+  const CascadeLayout c = cascade_layout(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                         max_context_len, prefix_blocks);
+  if (!workspace || workspace_bytes < c.total || !aligned16(workspace)) return PA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ints = reinterpret_cast<int32_t*>(ws + c.ints);
+  float* o1 = reinterpret_cast<float*>(ws + c.out1);
+  float* o2 = reinterpret_cast<float*>(ws + c.out2);
+  float* l1 = reinterpret_cast<float*>(ws + c.lse1);
+  float* l2 = reinterpret_cast<float*>(ws + c.lse2);
+  const int prefix_tokens = prefix_blocks * block_size;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pa::launch_cascade_prep(context_lens, num_seqs, prefix_tokens, max_context_len, ints,
+                              ints + 2, ints + 3, st) != hipSuccess)
+    return PA_ERR_HIP;
+  // the shared prefix: every sequence's query as one row over row 0's first blocks
+  rc = multiq_core(o1, q, k_cache, v_cache, block_tables, ints + 2, ints, 1, num_seqs, num_seqs,
+                   num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                   prefix_tokens, scale, 0, dtype, PA_F32, 0, c.mq_bytes ? ws + c.mq : nullptr,
+                   c.mq_bytes, stream, l1, none);
+  if (rc != PA_OK) return rc;
+  // each sequence's own tail: its table from entry prefix_blocks on (same row stride)
+  rc = decode_core(o2, q, k_cache, v_cache, block_tables + prefix_blocks, ints + 3, num_seqs,
+                   num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                   max_context_len - prefix_tokens, scale, dtype, PA_F32, 0,
+                   c.dec_bytes ? ws + c.dec : nullptr, c.dec_bytes, stream, l2, none);
+  if (rc != PA_OK) return rc;
+  hipError_t e = pa::launch_cascade_combine(out, o1, l1, o2, l2, (int64_t)num_seqs * num_heads,
+                                            head_dim, out_dtype, st);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

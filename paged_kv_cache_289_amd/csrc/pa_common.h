@@ -212,6 +212,9 @@ __device__ inline void group_sum_all(float (&x)[K]) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Log-sum-exp (log2 units) of a softmax state: running max m, sum l of 2^(z - m).
+__device__ inline float lse2_of(float m, float l) { return l > 0.f ? m + log2f(l) : kNegInf; }
+
 // Max / sum of a value and the one held by the lane 32 apart.  v_permlane32_swap
 // exchanges the upper half of one register with the lower half of the other;
 // applied to two copies of x, the two results hold x and its partner in every

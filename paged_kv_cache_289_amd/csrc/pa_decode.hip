@@ -434,6 +434,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
 #pragma unroll
           for (int e = 0; e < W::EPL; ++e)
             store_out(a.out, (head0 + h) * D + w.col * W::EPL + e, w.o[h][e] * inv, a.out_dtype);
+          if (a.lse && w.col == 0) a.lse[head0 + h] = lse2_of(w.m[h], w.l[h]);
         }
       } else {                        // a piece: partial for the merge
         const size_t slot = ((size_t)s * Hk + g + wid) * G;
@@ -484,6 +485,7 @@ __global__ __launch_bounds__(D) void split_merge_kernel(const AttnArgs a) {
   const size_t oidx = ((size_t)s * H + hq) * D + d;
   if (min(max(Lraw, 0), a.max_context_len) == 0) {
     store_out(a.out, oidx, 0.f, a.out_dtype);
+    if (a.lse && d == 0) a.lse[(size_t)s * H + hq] = kNegInf;
     return;
   }
   const int nb = p1 - p0;
@@ -524,6 +526,7 @@ __global__ __launch_bounds__(D) void split_merge_kernel(const AttnArgs a) {
     M = mx;
   }
   store_out(a.out, oidx, den > 0.f ? num / den : 0.f, a.out_dtype);
+  if (a.lse && d == 0) a.lse[(size_t)s * H + hq] = lse2_of(M, den);
 }
 
 // ---------------------------------------------------------------------------
@@ -560,6 +563,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const AttnAr
   if (n_parts == 0) {  // empty context: zero output rows, written by partition 0
     if (p == 0)
       for (int i = tid; i < G * D; i += kThreads) store_out(a.out, head0 * D + i, 0.f, a.out_dtype);
+    if (p == 0 && a.lse && tid < G) a.lse[head0 + tid] = kNegInf;
     return;
   }
   if (p >= n_parts) return;
@@ -610,6 +614,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const AttnAr
     const size_t hh = head0 + h;
     if (final_out) {
       store_out(a.out, hh * D + d, den > 0.f ? num / den : 0.f, a.out_dtype);
+      if (a.lse && d == 0) a.lse[hh] = lse2_of(mx, den);
     } else {
       const size_t slot = hh * a.max_parts + p;
       a.ws_o[slot * D + d] = num;
@@ -672,6 +677,7 @@ __global__ __launch_bounds__(D) void merge_kernel(const AttnArgs a) {
     M = mx;
   }
   store_out(a.out, hh * D + d, den > 0.f ? num / den : 0.f, a.out_dtype);
+  if (a.lse && d == 0) a.lse[hh] = lse2_of(M, den);
 }
 
 // ---------------------------------------------------------------------------

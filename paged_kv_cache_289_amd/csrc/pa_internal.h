@@ -57,6 +57,9 @@ struct AttnArgs {
   float scale_log2;          // scale * log2(e): scores are kept in log2 units
   // balanced-split decode (plan != nullptr)
   int* plan;                 // [2 + S + 1]: chunk, total items, block prefix sums
+  // optional: per (row, query head) log-sum-exp of the scores in log2 units,
+  // m + log2(l) (-inf for a row with no visible key), written with the output
+  float* lse;
   int chunk_blocks;          // items per wave (0: split evenly over the launch)
   int split_workgroups;      // workgroups launched
 };
@@ -108,6 +111,14 @@ hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
                               int elem_bytes, hipStream_t stream);
+
+hipError_t launch_cascade_prep(const int32_t* context_lens, int num_seqs, int prefix_tokens,
+                               int max_context_len, int32_t* q_offsets, int32_t* prefix_len,
+                               int32_t* tail_lens, hipStream_t stream);
+
+hipError_t launch_cascade_combine(void* out, const float* o1, const float* lse1, const float* o2,
+                                  const float* lse2, int64_t rows, int head_dim, int out_dtype,
+                                  hipStream_t stream);
 
 hipError_t launch_check(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                         int block_size, int num_blocks, int max_blocks_per_seq,

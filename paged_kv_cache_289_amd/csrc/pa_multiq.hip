@@ -151,6 +151,7 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
   if (L == 0) {  // nothing visible: zero rows, written once
     if (p == 0 && (ROWS || wave == 0) && row_ok)
       for (int d = hh * (D / 2); d < (hh + 1) * (D / 2); ++d) store_out(a.out, out_row * D + d, 0.f, a.out_dtype);
+    if (p == 0 && (ROWS || wave == 0) && row_ok && a.lse && hh == 0) a.lse[out_row] = kNegInf;
     return;
   }
   if (tok0 >= l_wg_max) return;        // no row of this workgroup sees this partition
@@ -443,6 +444,7 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         store_out(a.out, out_row * D + 32 * db + tile_token(v, hh), o[db][v] * inv, a.out_dtype);
+    if (a.lse && hh == 0) a.lse[out_row] = lse2_of(m_run, l_run);
   } else if (p < parts_row) {
     const size_t slot = out_row * a.max_parts + p;
     float* po = a.ws_o + slot * D;

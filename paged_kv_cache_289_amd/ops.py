@@ -36,6 +36,9 @@ SIGNATURES = {
     "paged_attn_default_partition": (_I, [_I, _I, _I, _I, _I, _I]),
     "paged_attn_set_kernel_events": (_I, [_P, _P]),
     "paged_attn_status_string": (ctypes.c_char_p, [_I]),
+    "paged_attn_shared_prefix_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "paged_attn_decode_shared_prefix": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                             _I, _I, _F, _I, _I, _P, _Z, _P]),
     "paged_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "paged_kv_copy_blocks": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "paged_pool_create": (_P, [_I, _I]),
@@ -183,6 +186,55 @@ def multiq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                _stream(stream))
     _check("paged_attn_multiq", rc)
     return out
+
+
+def shared_prefix_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                 max_context_len, prefix_blocks) -> int:
+    return int(LIB.paged_attn_shared_prefix_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                           head_dim, block_size, max_context_len,
+                                                           prefix_blocks))
+
+
+def _shared_prefix_args(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                        prefix_blocks, out, workspace, stream):
+    S, H, D = q.shape
+    NB, Hk, B, _ = k_cache.shape
+    need = shared_prefix_workspace_size(S, H, Hk, D, B, max_context_len, prefix_blocks)
+    workspace, wbytes = _workspace(need, q.device, workspace)
+    args = [_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), S, H, Hk, D, B, NB, block_tables.shape[1], int(max_context_len),
+            int(prefix_blocks), ctypes.c_float(scale), _dtype(q), _dtype(out), _ptr(workspace),
+            ctypes.c_size_t(wbytes), _stream(stream)]
+    return args, workspace
+
+
+def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                         max_context_len: int, prefix_blocks: int,
+                         out: Optional[torch.Tensor] = None, out_dtype=None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """:func:`decode` for tables that all start with the same ``prefix_blocks`` blocks
+    (and contexts that cover them): the prefix is attended once for all sequences."""
+    _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                 context_lens=context_lens, out=out)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    args, workspace = _shared_prefix_args(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                          max_context_len, prefix_blocks, out, workspace, stream)
+    _check("paged_attn_decode_shared_prefix", LIB.paged_attn_decode_shared_prefix(*args))
+    return out
+
+
+def prepare_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                 max_context_len, prefix_blocks, out, workspace=None,
+                                 stream=None) -> "PreparedCall":
+    """Check and marshal a :func:`decode_shared_prefix` call once."""
+    _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                 context_lens=context_lens, out=out)
+    args, workspace = _shared_prefix_args(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                          max_context_len, prefix_blocks, out, workspace, stream)
+    return PreparedCall("paged_attn_decode_shared_prefix", args, 2,
+                        (q, k_cache, v_cache, block_tables, context_lens, out, workspace))
 
 
 def gather(k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,

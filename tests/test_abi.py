@@ -122,3 +122,36 @@ def test_workspace_size_formula():
     assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 24) == 0     # rejected
     assert ops.default_partition(64, 32, 8, 16, 4096, 1) % 16 == 0
     assert ops.default_partition(1, 32, 8, 16, 4608, 512) % 32 == 0
+
+
+def _shared(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tbl=FAKE, lens=FAKE, S=4, H=32, Hk=8, D=128, B=16,
+             NB=100, mbs=64, maxctx=1024, P=8, scale=0.088, dt=ops.PA_BF16, odt=ops.PA_BF16,
+             ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return ops.LIB.paged_attn_decode_shared_prefix(
+        a["out"], a["q"], a["k"], a["v"], a["tbl"], a["lens"], a["S"], a["H"], a["Hk"], a["D"],
+        a["B"], a["NB"], a["mbs"], a["maxctx"], a["P"], a["scale"], a["dt"], a["odt"], a["ws"],
+        a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(P=-1), ops.PA_ERR_SHAPE),
+    (dict(P=65), ops.PA_ERR_SHAPE),
+    (dict(P=8, maxctx=100), ops.PA_ERR_SHAPE),
+    (dict(q=None), ops.PA_ERR_NULL),
+    (dict(wsb=16), ops.PA_ERR_WORKSPACE),
+    (dict(ws=None), ops.PA_ERR_WORKSPACE),
+    (dict(H=30), ops.PA_ERR_SHAPE),
+    (dict(S=0), ops.PA_OK),
+])
+def test_shared_prefix_rejects_bad_arguments(kw, code):
+    assert _shared(**kw) == code
+
+
+def test_shared_prefix_workspace_size():
+    full = ops.shared_prefix_workspace_size(256, 32, 8, 128, 16, 6144, 128)
+    assert full > ops.workspace_size(256, 256, 1, 32, 8, 128, 16, 6144)
+    assert ops.shared_prefix_workspace_size(256, 32, 8, 128, 16, 6144, 0) == \
+        ops.workspace_size(256, 256, 1, 32, 8, 128, 16, 6144)
+    assert ops.shared_prefix_workspace_size(4, 32, 8, 128, 16, 100, 8) == 0   # prefix > context
