@@ -471,7 +471,8 @@ def main():
         ach = basis / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBPS, 4)}
-    roof["traffic"] = measured_traffic(st.name, res["source_hash"])
+    roof["traffic"] = measured_traffic(st.name + ("_cascade" if a.cascade else ""),
+                                       res["source_hash"])
     roof["kernel"] = ("shared-prefix cascade, whole call (prep, prefix multi-query + merge, "
                       "tail decode + merge, combine)" if a.cascade else
                       "multi-query main kernel" if is_multiq else "decode split kernel")

@@ -309,7 +309,7 @@ int multiq_core(void* out, const void* q, const void* k_cache, const void* v_cac
                 int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                 int max_blocks_per_seq, int max_context_len, float scale, int causal, int dtype,
                 int out_dtype, int partition_tokens, void* workspace, size_t workspace_bytes,
-                pa_stream_t stream, float* lse, const pa::KernelEvents& ev) {
+                pa_stream_t stream, float* lse, const pa::KernelEvents& ev, int no_merge = 0) {
   int rc = check_attn_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                              max_blocks_per_seq, max_context_len, dtype, out_dtype,
                              partition_tokens, scale);
@@ -353,6 +353,7 @@ int multiq_core(void* out, const void* q, const void* k_cache, const void* v_cac
   a.out_dtype = out_dtype;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.lse = lse;
+  a.no_merge = no_merge;
   hipError_t e = pa::launch_multiq(dtype, head_dim, block_size, a.group, num_seqs, a,
                                    static_cast<hipStream_t>(stream), ev);
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
@@ -492,20 +493,26 @@ int paged_attn_decode_shared_prefix(void* out, const void* q, const void* k_cach
   if (pa::launch_cascade_prep(context_lens, num_seqs, prefix_tokens, max_context_len, ints,
                               ints + 2, ints + 3, st) != hipSuccess)
     return PA_ERR_HIP;
-  // the shared prefix: every sequence's query as one row over row 0's first blocks
+  // the shared prefix: every sequence's query as one row over row 0's first blocks;
+  // with several partitions their partials stay in the workspace for the combine
+  const int part = resolve_partition(0, 1, num_heads, num_kv_heads, block_size, prefix_tokens,
+                                     num_seqs);
+  const int n_parts = std::max(1, ceil_div(prefix_tokens, part));
   rc = multiq_core(o1, q, k_cache, v_cache, block_tables, ints + 2, ints, 1, num_seqs, num_seqs,
                    num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                    prefix_tokens, scale, 0, dtype, PA_F32, 0, c.mq_bytes ? ws + c.mq : nullptr,
-                   c.mq_bytes, stream, l1, none);
+                   c.mq_bytes, stream, l1, none, /*no_merge=*/1);
   if (rc != PA_OK) return rc;
+  const float* p_ml = reinterpret_cast<const float*>(ws + c.mq);
+  const float* p_o = p_ml + (size_t)num_seqs * num_heads * n_parts * 2;
   // each sequence's own tail: its table from entry prefix_blocks on (same row stride)
   rc = decode_core(o2, q, k_cache, v_cache, block_tables + prefix_blocks, ints + 3, num_seqs,
                    num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                    max_context_len - prefix_tokens, scale, dtype, PA_F32, 0,
                    c.dec_bytes ? ws + c.dec : nullptr, c.dec_bytes, stream, l2, none);
   if (rc != PA_OK) return rc;
-  hipError_t e = pa::launch_cascade_combine(out, o1, l1, o2, l2, (int64_t)num_seqs * num_heads,
-                                            head_dim, out_dtype, st);
+  hipError_t e = pa::launch_cascade_combine(out, p_ml, p_o, n_parts, n_parts, o1, l1, o2, l2,
+                                            num_seqs, num_heads, head_dim, out_dtype, st);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -32,22 +32,65 @@ __global__ __launch_bounds__(256) void cascade_prep_kernel(const int32_t* __rest
   }
 }
 
-// One thread per output element: the log-sum-exp combination of the two parts.
-__global__ __launch_bounds__(256) void cascade_combine_kernel(
-    void* __restrict__ out, const float* __restrict__ o1, const float* __restrict__ lse1,
-    const float* __restrict__ o2, const float* __restrict__ lse2, int64_t n, int D,
-    int out_dtype) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int64_t r = i / D;
-  const float a = lse1[r], b = lse2[r];
-  const float M = fmaxf(a, b);
-  if (M == kNegInf) {
-    store_out(out, i, 0.f, out_dtype);
+// One workgroup per (sequence, query head), thread d owns dim d.  The prefix
+// pass left n_parts partition partials (max m_p, sum l_p, unnormalized o_p, in
+// log2 units) when it had several, else its normalized output o1 and lse1 (one
+// "partial" with m = lse1, l = 1); the tail pass left its normalized output o2
+// and lse2 (a partial with m = lse2, l = 1).  All are folded in one
+// log-sum-exp: out = sum 2^(m - M) o / sum 2^(m - M) l.
+template <int D>
+__global__ __launch_bounds__(D) void cascade_combine_kernel(
+    void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
+    int max_parts, int n_parts, const float* __restrict__ o1, const float* __restrict__ lse1,
+    const float* __restrict__ o2, const float* __restrict__ lse2, int out_dtype) {
+  const int64_t r = (int64_t)blockIdx.x * gridDim.y + blockIdx.y;   // (sequence, head) row
+  const int d = threadIdx.x;
+  constexpr int kMax = 16;   // partials loaded per round
+  float M = lse2[r], num = 0.f, den = 0.f;
+  const float t_o = o2[r * D + d];
+  if (n_parts <= 1) {
+    const float m1 = lse1[r];
+    const float mx = fmaxf(M, m1);
+    if (mx == kNegInf) {
+      store_out(out, r * D + d, 0.f, out_dtype);
+      return;
+    }
+    const float w1 = fast_exp2(m1 - mx), w2 = fast_exp2(M - mx);
+    store_out(out, r * D + d, (w1 * o1[r * D + d] + w2 * t_o) / (w1 + w2), out_dtype);
     return;
   }
-  const float w1 = fast_exp2(a - M), w2 = fast_exp2(b - M);
-  store_out(out, i, (w1 * o1[i] + w2 * o2[i]) / (w1 + w2), out_dtype);
+  // start from the tail's part, then fold the prefix partials in rounds
+  const bool tail = M != kNegInf;
+  num = tail ? t_o : 0.f;
+  den = tail ? 1.f : 0.f;
+  const float* ml = ws_ml + 2 * r * max_parts;
+  const float* po = ws_o + r * max_parts * D + d;
+  for (int p0 = 0; p0 < n_parts; p0 += kMax) {
+    float pm[kMax], pl[kMax], pv[kMax];
+#pragma unroll
+    for (int k = 0; k < kMax; ++k) {
+      const int pk = min(p0 + k, n_parts - 1);
+      pm[k] = ml[2 * pk];
+      pl[k] = ml[2 * pk + 1];
+      pv[k] = po[(size_t)pk * D];
+    }
+    float mx = M;
+#pragma unroll
+    for (int k = 0; k < kMax; ++k)
+      if (p0 + k < n_parts) mx = fmaxf(mx, pm[k]);
+    const float ms = (mx == kNegInf) ? 0.f : mx;
+    const float rs = fast_exp2(M - ms);
+    num *= rs;
+    den *= rs;
+#pragma unroll
+    for (int k = 0; k < kMax; ++k) {
+      const float wt = (p0 + k < n_parts) ? fast_exp2(pm[k] - ms) : 0.f;
+      num = __builtin_fmaf(wt, pv[k], num);
+      den = __builtin_fmaf(wt, pl[k], den);
+    }
+    M = mx;
+  }
+  store_out(out, r * D + d, den > 0.f ? num / den : 0.f, out_dtype);
 }
 
 hipError_t launch_cascade_prep(const int32_t* context_lens, int num_seqs, int prefix_tokens,
@@ -59,12 +102,17 @@ hipError_t launch_cascade_prep(const int32_t* context_lens, int num_seqs, int pr
   return hipGetLastError();
 }
 
-hipError_t launch_cascade_combine(void* out, const float* o1, const float* lse1, const float* o2,
-                                  const float* lse2, int64_t rows, int head_dim, int out_dtype,
-                                  hipStream_t st) {
-  const int64_t n = rows * head_dim;
-  hipLaunchKernelGGL(cascade_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     out, o1, lse1, o2, lse2, n, head_dim, out_dtype);
+hipError_t launch_cascade_combine(void* out, const float* ws_ml, const float* ws_o, int max_parts,
+                                  int n_parts, const float* o1, const float* lse1, const float* o2,
+                                  const float* lse2, int num_seqs, int num_heads, int head_dim,
+                                  int out_dtype, hipStream_t st) {
+  const dim3 grid(num_seqs, num_heads);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(cascade_combine_kernel<64>, grid, dim3(64), 0, st, out, ws_ml, ws_o,
+                       max_parts, n_parts, o1, lse1, o2, lse2, out_dtype);
+  else
+    hipLaunchKernelGGL(cascade_combine_kernel<128>, grid, dim3(128), 0, st, out, ws_ml, ws_o,
+                       max_parts, n_parts, o1, lse1, o2, lse2, out_dtype);
   return hipGetLastError();
 }
 

@@ -62,6 +62,9 @@ struct AttnArgs {
   float* lse;
   int chunk_blocks;          // items per wave (0: split evenly over the launch)
   int split_workgroups;      // workgroups launched
+  // multi-token calls: leave the partition partials in the workspace for the
+  // caller's own merge instead of launching merge_kernel
+  int no_merge;
 };
 
 // Optional events recorded right around a call's main kernel (profiling aid).
@@ -116,9 +119,13 @@ hipError_t launch_cascade_prep(const int32_t* context_lens, int num_seqs, int pr
                                int max_context_len, int32_t* q_offsets, int32_t* prefix_len,
                                int32_t* tail_lens, hipStream_t stream);
 
-hipError_t launch_cascade_combine(void* out, const float* o1, const float* lse1, const float* o2,
-                                  const float* lse2, int64_t rows, int head_dim, int out_dtype,
-                                  hipStream_t stream);
+// Final rows of the shared-prefix decode: the prefix pass's n_parts partition
+// partials (or, with one partition, its normalized output o1 and lse1) and the
+// tail pass's normalized output o2 and lse2, combined by log-sum-exp.
+hipError_t launch_cascade_combine(void* out, const float* ws_ml, const float* ws_o, int max_parts,
+                                  int n_parts, const float* o1, const float* lse1, const float* o2,
+                                  const float* lse2, int num_seqs, int num_heads, int head_dim,
+                                  int out_dtype, hipStream_t stream);
 
 hipError_t launch_check(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                         int block_size, int num_blocks, int max_blocks_per_seq,

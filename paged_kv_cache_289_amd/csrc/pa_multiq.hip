@@ -486,7 +486,7 @@ static hipError_t launch_mfma_t(int num_seqs, const AttnArgs& a, hipStream_t st,
   const hipError_t e =
       rows ? launch_main(multiq_mfma_rows_kernel<DT, D, B>, grid, dim3(kThreads), 0, st, ev, a)
            : launch_main(multiq_mfma_kernel<DT, D, B>, grid, dim3(kThreads), 0, st, ev, a);
-  if (e != hipSuccess || a.max_parts <= 1) return e;
+  if (e != hipSuccess || a.max_parts <= 1 || a.no_merge) return e;
   return launch_merge(D, num_seqs, a, st);
 }
 

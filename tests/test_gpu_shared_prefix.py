@@ -58,13 +58,15 @@ def test_shared_prefix_edges():
 
 
 def test_shared_prefix_long_prefix_many_rows():
-    """A long shared prefix (several partitions of the prefix pass) under short tails."""
-    st = W.shared_prefix_mix(5, num_seqs=40, prefix_blocks=150, tail_median=20, tail_max=100)
+    """A long shared prefix under short tails: the prefix pass has more partitions
+    than the combine folds in one round (4,800 tokens in 256-token partitions)."""
+    st = W.shared_prefix_mix(5, num_seqs=40, prefix_blocks=300, tail_median=20, tail_max=100)
     vals = W.host_values(st)
     t = U.upload(st, vals)
     seqs = [0, 7, 39]
     want = U.oracle_decode(st, vals, seqs=seqs)
-    U.assert_close(_run(st, t, 150, torch.float32), want, "bf16", "P=150", rows=seqs)
+    U.assert_close(_run(st, t, 300, torch.float32), want, "bf16", "P=300", rows=seqs)
+    U.assert_close(_run(st, t, 300), want, "bf16", "P=300 bf16 out", rows=seqs)
 
 
 def test_full_shared_prefix_mix_cascade():
