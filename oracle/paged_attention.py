@@ -59,7 +59,43 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if dtype == "f64":
         return np.asarray(x, dtype=np.float64)
+    if dtype == "fp8e4m3":
+        return widen_fp8e4m3(x)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def widen_fp8e4m3(codes: np.ndarray) -> np.ndarray:
+    """Exact values of 8-bit floating-point codes in the E4M3 format with no
+    infinities (the OCP 8-bit format): sign bit, 4 exponent bits with bias 7, 3
+    mantissa bits.  Exponent field 0 holds the subnormals m/8 * 2^-6; the code
+    with all exponent and mantissa bits set is NaN."""
+    c = np.asarray(codes)
+    assert c.dtype == np.uint8, "fp8 arrays are uint8 codes"
+    c = c.astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def paged_decode_quant_kv(q: np.ndarray, q_dtype: str, k_cache: np.ndarray, v_cache: np.ndarray,
+                          kv_dtype: str, k_scale: float, v_scale: float, block_tables: np.ndarray,
+                          context_lens: np.ndarray, block_size: int, scale: float,
+                          seqs: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Decode over a cache stored in a reduced-precision format with one scale per
+    tensor: the keys are ``k_scale * widen(k)`` and the values ``v_scale * widen(v)``;
+    the query keeps its own type.  Otherwise the same gather and attention."""
+    S, H, D = q.shape
+    out = np.zeros((S, H, D), np.float64)
+    idx = list(range(S)) if seqs is None else list(seqs)
+    for s, (Ks, Vs) in zip(idx, gather_contiguous(k_cache, v_cache, block_tables, context_lens,
+                                                  block_size, idx)):
+        L = int(context_lens[s])
+        out[s:s + 1] = attend_rows(widen(q[s:s + 1], q_dtype), k_scale * widen(Ks, kv_dtype),
+                                   v_scale * widen(Vs, kv_dtype), scale, [L])
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -127,3 +127,46 @@ def test_gather_is_bit_exact_copy_of_pool_slots():
             b = st.block_tables[s, t // 8]
             assert np.array_equal(K[t], vals["k_cache"][b, :, t % 8, :])
             assert np.array_equal(V[t], vals["v_cache"][b, :, t % 8, :])
+
+
+# --------------------------------------------------------------------------
+# 8-bit floating-point KV (E4M3)
+# --------------------------------------------------------------------------
+
+def test_fp8_widening_matches_torch_for_every_code():
+    """The format definition against torch's own float8_e4m3fn conversion."""
+    import torch
+    import oracle.paged_attention as OP
+    codes = np.arange(256, dtype=np.uint8)
+    mine = OP.widen(codes, "fp8e4m3")
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+
+
+@pytest.mark.parametrize("code,value", [(0x38, 1.0), (0xB8, -1.0), (0x7E, 448.0),
+                                        (0x01, 2.0 ** -9), (0x08, 2.0 ** -6), (0x00, 0.0),
+                                        (0x3C, 1.5), (0x07, 7 * 2.0 ** -9)])
+def test_fp8_closed_forms(code, value):
+    import oracle.paged_attention as OP
+    assert OP.widen(np.array([code], np.uint8), "fp8e4m3")[0] == value
+
+
+def test_quant_kv_decode_applies_the_scales():
+    """Scaling K by c equals scaling the scores by c; scaling V by c scales the output."""
+    import oracle.paged_attention as OP
+    st = W.random_small(9, num_seqs=3, num_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+                        ctx_lo=5, ctx_hi=90, dtype="bf16")
+    vals = W.host_values(st)
+    rng = np.random.default_rng(9)
+    k8 = rng.integers(0, 256, size=vals["k_cache"].shape, dtype=np.uint8)
+    v8 = rng.integers(0, 256, size=vals["v_cache"].shape, dtype=np.uint8)
+    k8[(k8 & 0x7F) == 0x7F] = 0x38                     # no NaN codes
+    v8[(v8 & 0x7F) == 0x7F] = 0x38
+    k8[((k8 >> 3) & 15) >= 12] &= 0xA7                  # keep scores moderate
+    a = OP.paged_decode_quant_kv(vals["q"], "bf16", k8, v8, "fp8e4m3", 0.25, 3.0, st.block_tables,
+                                 st.context_lens, 16, 0.125)
+    b = OP.paged_decode_quant_kv(vals["q"], "bf16", k8, v8, "fp8e4m3", 1.0, 1.0, st.block_tables,
+                                 st.context_lens, 16, 0.125 * 0.25)
+    assert np.max(np.abs(a - 3.0 * b)) <= 1e-12
