@@ -64,7 +64,10 @@ typedef enum {
   PA_ERR_INVALID = -7      /* unknown or released sequence id, bad block id    */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* PA_FP8_E4M3: 8-bit floating-point codes (sign, 4 exponent bits with bias 7,
+   3 mantissa bits, no infinities; the all-ones magnitude is NaN), used only for
+   the K/V pools of paged_attn_decode_fp8kv. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Opaque to this header; it is a hipStream_t. */
 typedef void* pa_stream_t;
@@ -210,6 +213,33 @@ int paged_attn_decode_shared_prefix(void* out, const void* q, const void* k_cach
                                     int num_blocks, int max_blocks_per_seq, int max_context_len,
                                     int prefix_blocks, float scale, int dtype, int out_dtype,
                                     void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * Decode over an 8-bit KV cache.  The same call as paged_attn_decode, with
+ * k_cache and v_cache holding PA_FP8_E4M3 codes (1 byte per element, the same
+ * [num_blocks][num_kv_heads][block_size][head_dim] layout) and one scale per
+ * tensor: the keys are k_scale * (decoded code) and the values v_scale *
+ * (decoded code).  Half the K/V bytes of a 16-bit cache.  The pages apply
+ * "fewer bits, faster memory access" to weights ("Scaling inference with
+ * vLLM", quantization paragraph); here it is applied to the cache the decode
+ * streams.
+ *
+ * q is bf16 [num_seqs][num_heads][head_dim] (converted to f16 in the kernel:
+ * exact for |q| in f16's normal range); out_dtype is PA_F32 or PA_BF16.
+ * Accumulation is fp32.  Codes are widened exactly; the NaN codes are not
+ * supported.  Supported: head_dim 128 with block_size 8/16/32, head_dim 64
+ * with block_size 16/32, groups num_heads / num_kv_heads of at most 8.
+ * partition_tokens, the workspace (paged_attn_workspace_size(...) for the same
+ * shapes and partition_tokens) and the errors are as for paged_attn_decode,
+ * plus PA_ERR_SHAPE for k_scale or v_scale not finite and positive.
+ */
+int paged_attn_decode_fp8kv(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                            int block_size, int num_blocks, int max_blocks_per_seq,
+                            int max_context_len, float scale, float k_scale, float v_scale,
+                            int out_dtype, int partition_tokens, void* workspace,
+                            size_t workspace_bytes, pa_stream_t stream);
 
 /* Static description of a status code. */
 const char* paged_attn_status_string(int status);

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "pa_internal.h"
 
@@ -216,16 +217,19 @@ int decode_core(void* out, const void* q, const void* k_cache, const void* v_cac
                 int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                 int max_blocks_per_seq, int max_context_len, float scale, int dtype, int out_dtype,
                 int partition_tokens, void* workspace, size_t workspace_bytes, pa_stream_t stream,
-                float* lse, const pa::KernelEvents& ev) {
+                float* lse, const pa::KernelEvents& ev, float out_scale = 1.f) {
+  // (8-bit caches come with bf16 queries: the query type is what the checks see)
   int rc = check_attn_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                             max_blocks_per_seq, max_context_len, dtype, out_dtype,
-                             partition_tokens, scale);
+                             max_blocks_per_seq, max_context_len,
+                             dtype == PA_FP8_E4M3 ? PA_BF16 : dtype, out_dtype, partition_tokens,
+                             scale);
   if (rc != PA_OK) return rc;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
 
   pa::AttnArgs a{};
+  a.out_scale = out_scale;
   a.out = out;
   a.q = q;
   a.k_cache = k_cache;
@@ -352,6 +356,7 @@ int multiq_core(void* out, const void* q, const void* k_cache, const void* v_cac
   a.causal = causal ? 1 : 0;
   a.out_dtype = out_dtype;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_scale = 1.f;
   a.lse = lse;
   a.no_merge = no_merge;
   hipError_t e = pa::launch_multiq(dtype, head_dim, block_size, a.group, num_seqs, a,
@@ -514,6 +519,29 @@ int paged_attn_decode_shared_prefix(void* out, const void* q, const void* k_cach
   hipError_t e = pa::launch_cascade_combine(out, p_ml, p_o, n_parts, n_parts, o1, l1, o2, l2,
                                             num_seqs, num_heads, head_dim, out_dtype, st);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int paged_attn_decode_fp8kv(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                            int block_size, int num_blocks, int max_blocks_per_seq,
+                            int max_context_len, float scale, float k_scale, float v_scale,
+                            int out_dtype, int partition_tokens, void* workspace,
+                            size_t workspace_bytes, pa_stream_t stream) {
+  if (!(std::isfinite(k_scale) && std::isfinite(v_scale)) || !(k_scale > 0.f) ||
+      !(v_scale > 0.f))
+    return PA_ERR_SHAPE;
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (head_dim == 64 && block_size == 8) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads > 0 && num_heads % num_kv_heads == 0 && num_heads / num_kv_heads > 8)
+    return PA_ERR_UNSUPPORTED;
+  // the tensor scales go into the score scale and the output factor
+  const float qk = scale * k_scale;
+  if (!std::isfinite(qk)) return PA_ERR_SHAPE;
+  return decode_core(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                     max_context_len, qk, PA_FP8_E4M3, out_dtype, partition_tokens, workspace,
+                     workspace_bytes, stream, nullptr, t_events, v_scale);
 }
 
 int paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,

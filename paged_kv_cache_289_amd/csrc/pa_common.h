@@ -26,6 +26,14 @@ constexpr float kMaxInit = -1e30f;
 template <int DT> struct Elem;
 
 template <> struct Elem<PA_F32> {
+  typedef uint4 QVec;   // the query in the same type, one 16-byte vector
+  __device__ static inline QVec load_q(const void* q, size_t idx) {
+    return reinterpret_cast<const uint4*>(q)[idx / kPerVec];
+  }
+  __device__ static inline QVec zero_q() { return make_uint4(0, 0, 0, 0); }
+  __device__ static inline void flip_q(QVec& v) {
+    v.x ^= 0x80000000u; v.y ^= 0x80000000u; v.z ^= 0x80000000u; v.w ^= 0x80000000u;
+  }
   static constexpr int kBytes = 4;
   static constexpr int kPerVec = 4;
   // partial dot product of the 4 elements held in one vector
@@ -53,6 +61,14 @@ __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 template <> struct Elem<PA_BF16> {
+  typedef uint4 QVec;   // the query in the same type, one 16-byte vector
+  __device__ static inline QVec load_q(const void* q, size_t idx) {
+    return reinterpret_cast<const uint4*>(q)[idx / kPerVec];
+  }
+  __device__ static inline QVec zero_q() { return make_uint4(0, 0, 0, 0); }
+  __device__ static inline void flip_q(QVec& v) {
+    v.x ^= 0x80008000u; v.y ^= 0x80008000u; v.z ^= 0x80008000u; v.w ^= 0x80008000u;
+  }
   static constexpr int kBytes = 2;
   static constexpr int kPerVec = 8;
   __device__ static inline float dot2(uint32_t a, uint32_t b, float acc) {
@@ -83,6 +99,14 @@ template <> struct Elem<PA_BF16> {
 };
 
 template <> struct Elem<PA_F16> {
+  typedef uint4 QVec;   // the query in the same type, one 16-byte vector
+  __device__ static inline QVec load_q(const void* q, size_t idx) {
+    return reinterpret_cast<const uint4*>(q)[idx / kPerVec];
+  }
+  __device__ static inline QVec zero_q() { return make_uint4(0, 0, 0, 0); }
+  __device__ static inline void flip_q(QVec& v) {
+    v.x ^= 0x80008000u; v.y ^= 0x80008000u; v.z ^= 0x80008000u; v.w ^= 0x80008000u;
+  }
   static constexpr int kBytes = 2;
   static constexpr int kPerVec = 8;
   __device__ static inline float dot2(uint32_t a, uint32_t b, float acc) {
@@ -111,6 +135,77 @@ template <> struct Elem<PA_F16> {
   }
   __device__ static inline void to_float(const uint4& v, float* f) {
     pair(v.x, f); pair(v.y, f + 2); pair(v.z, f + 4); pair(v.w, f + 6);
+  }
+};
+
+// 8-bit E4M3 keys and values, with bf16 queries.  A 16-byte vector holds 16
+// codes.  gfx950 widens two codes per instruction: v_cvt_scalef32_pk_f16_fp8
+// to an f16 pair (every E4M3 value is exact in f16) for QK as v_dot2_f32_f16
+// against the query held as f16 pairs, and v_cvt_pk_f32_fp8 to two fp32
+// values for PV.  The NaN codes are not supported.
+struct Fp8Q {
+  uint32_t w[8];   // 16 query values as f16 pairs
+};
+
+template <> struct Elem<PA_FP8_E4M3> {
+  static constexpr int kBytes = 1;
+  static constexpr int kPerVec = 16;
+  typedef Fp8Q QVec;
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  acc, false);
+  }
+  // codes 0, 1 (hi = false) or 2, 3 (hi = true) of a dword as an f16 pair
+  template <bool HI>
+  __device__ static inline uint32_t f16_pair(uint32_t x) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HI));
+  }
+  __device__ static inline float dot0(const QVec& q, const uint4& k) {
+    const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = dot2(q.w[2 * i], f16_pair<false>(kw[i]), acc);
+      acc = dot2(q.w[2 * i + 1], f16_pair<true>(kw[i]), acc);
+    }
+    return acc;
+  }
+  __device__ static inline void to_float(const uint4& v, float* f) {
+    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(vw[i], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(vw[i], true);
+      f[4 * i] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    }
+  }
+  // 16 bf16 query values starting at element `idx` (16-element aligned), as f16
+  // pairs (rounded to nearest; bf16 values within f16's range convert exactly)
+  __device__ static inline QVec load_q(const void* q, size_t idx) {
+    const uint4* p = reinterpret_cast<const uint4*>(q) + idx / 8;
+    const uint4 a = p[0], b = p[1];
+    const uint32_t src[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    QVec r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      typedef float f2_t __attribute__((ext_vector_type(2)));
+      const f2_t f = {bf16_lo(src[i]), bf16_hi(src[i])};
+      r.w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+    }
+    return r;
+  }
+  __device__ static inline QVec zero_q() {
+    QVec r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.w[i] = 0u;
+    return r;
+  }
+  __device__ static inline void flip_q(QVec& q) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q.w[i] ^= 0x80008000u;
   }
 };
 

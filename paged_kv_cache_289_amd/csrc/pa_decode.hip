@@ -78,7 +78,7 @@ struct DecodeWave {
   static constexpr int kScoresPerLane = (kScores + 15) / 16;
 
   int row, col;                 // token row within a load, 16-byte column
-  uint4 qv[GP];
+  typename E::QVec qv[GP];
   float m[GP], l[GP], o[GP][EPL];
   float m_lane, l_lane;         // kOwnExp: this lane's head (col % GP)
 
@@ -87,13 +87,10 @@ struct DecodeWave {
   // query vectors of heads head0 .. head0 + G - 1 (zero for padded heads),
   // sign-flipped when the scale is negative (exact in every storage type)
   __device__ void load_q(const void* q, size_t head0, int G, float scale_log2) {
-    const uint4* qs = reinterpret_cast<const uint4*>(q);
-    const uint32_t flip = scale_log2 < 0.f ? (E::kBytes == 4 ? 0x80000000u : 0x80008000u) : 0u;
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
-      uint4 v = (h < G) ? qs[((head0 + h) * D) / EPL + col] : make_uint4(0, 0, 0, 0);
-      v.x ^= flip; v.y ^= flip; v.z ^= flip; v.w ^= flip;
-      qv[h] = v;
+      qv[h] = (h < G) ? E::load_q(q, (head0 + h) * D + (size_t)col * EPL) : E::zero_q();
+      if (scale_log2 < 0.f) E::flip_q(qv[h]);
     }
   }
 
@@ -430,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
           if (h >= G) break;
-          const float inv = w.l[h] > 0.f ? 1.f / w.l[h] : 0.f;
+          const float inv = w.l[h] > 0.f ? a.out_scale / w.l[h] : 0.f;
 #pragma unroll
           for (int e = 0; e < W::EPL; ++e)
             store_out(a.out, (head0 + h) * D + w.col * W::EPL + e, w.o[h][e] * inv, a.out_dtype);
@@ -525,7 +522,7 @@ __global__ __launch_bounds__(D) void split_merge_kernel(const AttnArgs a) {
     }
     M = mx;
   }
-  store_out(a.out, oidx, den > 0.f ? num / den : 0.f, a.out_dtype);
+  store_out(a.out, oidx, den > 0.f ? a.out_scale * num / den : 0.f, a.out_dtype);
   if (a.lse && d == 0) a.lse[(size_t)s * H + hq] = lse2_of(M, den);
 }
 
@@ -613,7 +610,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const AttnAr
     }
     const size_t hh = head0 + h;
     if (final_out) {
-      store_out(a.out, hh * D + d, den > 0.f ? num / den : 0.f, a.out_dtype);
+      store_out(a.out, hh * D + d, den > 0.f ? a.out_scale * num / den : 0.f, a.out_dtype);
       if (a.lse && d == 0) a.lse[hh] = lse2_of(mx, den);
     } else {
       const size_t slot = hh * a.max_parts + p;
@@ -676,7 +673,7 @@ __global__ __launch_bounds__(D) void merge_kernel(const AttnArgs a) {
     }
     M = mx;
   }
-  store_out(a.out, hh * D + d, den > 0.f ? num / den : 0.f, a.out_dtype);
+  store_out(a.out, hh * D + d, den > 0.f ? a.out_scale * num / den : 0.f, a.out_dtype);
   if (a.lse && d == 0) a.lse[hh] = lse2_of(M, den);
 }
 
@@ -737,10 +734,16 @@ static auto with_config(int dtype, int head_dim, int block_size, int group, F&& 
     if (group <= 2) return f(dt, d, b, std::integral_constant<int, 2>{});
     if (group <= 4) return f(dt, d, b, std::integral_constant<int, 4>{});
     if (group <= 8) return f(dt, d, b, std::integral_constant<int, 8>{});
-    return f(dt, d, b, std::integral_constant<int, 16>{});
+    // (8-bit caches stop at groups of 8: a lane's 16-element rows for 16 heads
+    // would not fit the register file; the host rejects them)
+    constexpr bool kNo16 = decltype(dt)::value == PA_FP8_E4M3;
+    return f(dt, d, b, std::integral_constant<int, kNo16 ? 8 : 16>{});
   };
   auto by_b = [&](auto dt, auto d) {
-    if (block_size == 8) return by_g(dt, d, std::integral_constant<int, 8>{});
+    // (8-bit codes at head_dim 64 fill 16 tokens per wave load, more than an
+    // 8-token block: the host rejects that pair, the 16-token instance stands in)
+    constexpr bool kNo8 = decltype(dt)::value == PA_FP8_E4M3 && decltype(d)::value == 64;
+    if (block_size == 8 && !kNo8) return by_g(dt, d, std::integral_constant<int, kNo8 ? 16 : 8>{});
     if (block_size == 16) return by_g(dt, d, std::integral_constant<int, 16>{});
     return by_g(dt, d, std::integral_constant<int, 32>{});
   };
@@ -750,6 +753,7 @@ static auto with_config(int dtype, int head_dim, int block_size, int group, F&& 
   };
   if (dtype == PA_F32) return by_d(std::integral_constant<int, PA_F32>{});
   if (dtype == PA_F16) return by_d(std::integral_constant<int, PA_F16>{});
+  if (dtype == PA_FP8_E4M3) return by_d(std::integral_constant<int, PA_FP8_E4M3>{});
   return by_d(std::integral_constant<int, PA_BF16>{});
 }
 

@@ -55,6 +55,7 @@ struct AttnArgs {
   int causal;
   int out_dtype;
   float scale_log2;          // scale * log2(e): scores are kept in log2 units
+  float out_scale;           // factor on every final output (1, or the V scale of 8-bit caches)
   // balanced-split decode (plan != nullptr)
   int* plan;                 // [2 + S + 1]: chunk, total items, block prefix sums
   // optional: per (row, query head) log-sum-exp of the scores in log2 units,

@@ -19,7 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedat
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = \
     0, -1, -2, -3, -4, -5
 PA_ERR_NO_BLOCKS, PA_ERR_INVALID = -6, -7
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 
 _TORCH_DT = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
@@ -39,6 +39,8 @@ SIGNATURES = {
     "paged_attn_shared_prefix_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "paged_attn_decode_shared_prefix": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                              _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "paged_attn_decode_fp8kv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                                     _F, _F, _I, _I, _P, _Z, _P]),
     "paged_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "paged_kv_copy_blocks": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "paged_pool_create": (_P, [_I, _I]),
@@ -234,6 +236,50 @@ def prepare_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens
     args, workspace = _shared_prefix_args(q, k_cache, v_cache, block_tables, context_lens, scale,
                                           max_context_len, prefix_blocks, out, workspace, stream)
     return PreparedCall("paged_attn_decode_shared_prefix", args, 2,
+                        (q, k_cache, v_cache, block_tables, context_lens, out, workspace))
+
+
+def _fp8kv_args(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                max_context_len, out, workspace, stream, partition_tokens=0):
+    assert k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8 and q.dtype == torch.bfloat16
+    S, H, D = q.shape
+    NB, Hk, B, _ = k_cache.shape
+    need = workspace_size(S, S, 1, H, Hk, D, B, max_context_len, partition_tokens)
+    workspace, wbytes = _workspace(need, q.device, workspace)
+    args = [_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), S, H, Hk, D, B, NB, block_tables.shape[1], int(max_context_len),
+            ctypes.c_float(scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale), _dtype(out),
+            int(partition_tokens), _ptr(workspace), ctypes.c_size_t(wbytes), _stream(stream)]
+    return args, workspace
+
+
+def decode_fp8kv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                 k_scale: float, v_scale: float, max_context_len: int,
+                 out: Optional[torch.Tensor] = None, out_dtype=None, partition_tokens: int = 0,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """:func:`decode` over an 8-bit E4M3 cache (uint8 code tensors ``[NB, Hk, B, D]``)
+    with per-tensor scales; ``q`` is bf16."""
+    _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                 context_lens=context_lens, out=out)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    args, workspace = _fp8kv_args(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                  k_scale, v_scale, max_context_len, out, workspace, stream,
+                                  partition_tokens)
+    _check("paged_attn_decode_fp8kv", LIB.paged_attn_decode_fp8kv(*args))
+    return out
+
+
+def prepare_decode_fp8kv(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                         v_scale, max_context_len, out, workspace=None,
+                         stream=None) -> "PreparedCall":
+    """Check and marshal a :func:`decode_fp8kv` call once."""
+    _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                 context_lens=context_lens, out=out)
+    args, workspace = _fp8kv_args(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                  k_scale, v_scale, max_context_len, out, workspace, stream)
+    return PreparedCall("paged_attn_decode_fp8kv", args, 2,
                         (q, k_cache, v_cache, block_tables, context_lens, out, workspace))
 
 
