@@ -46,17 +46,24 @@ int resolve_partition(int partition_tokens, int num_seqs, int num_heads, int num
                                             max_context_len, max_q_len);
 }
 
-// Partition-mode workspace: fp32 (max, sum) pairs [rows][H][P], then fp32
+// Partition-mode workspace: fp32 (max, sum) pairs [rows][H][P], padded to a
+// multiple of 4 floats so that the partial outputs after them start on a
+// 16-byte boundary (the kernels move them as 16-byte vectors), then fp32
 // partial outputs [rows][H][P][D].
+size_t partial_ml_floats(int rows, int num_heads, int max_parts) {
+  return ((size_t)rows * num_heads * max_parts * 2 + 3) / 4 * 4;
+}
+
 size_t workspace_bytes_for(int rows, int num_heads, int head_dim, int max_parts) {
   if (max_parts <= 1) return 0;
-  return (size_t)rows * num_heads * max_parts * ((size_t)head_dim + 2) * sizeof(float);
+  return (partial_ml_floats(rows, num_heads, max_parts) +
+          (size_t)rows * num_heads * max_parts * head_dim) * sizeof(float);
 }
 
 void split_workspace(void* ws, int rows, int num_heads, int max_parts, pa::AttnArgs* a) {
   float* base = static_cast<float*>(ws);
   a->ws_ml = base;
-  a->ws_o = base + (size_t)rows * num_heads * max_parts * 2;
+  a->ws_o = base + partial_ml_floats(rows, num_heads, max_parts);
 }
 
 // Balanced-split decode plan.  Work items are (sequence, KV head, block);
@@ -509,7 +516,7 @@ int paged_attn_decode_shared_prefix(void* out, const void* q, const void* k_cach
                    c.mq_bytes, stream, l1, none, /*no_merge=*/1);
   if (rc != PA_OK) return rc;
   const float* p_ml = reinterpret_cast<const float*>(ws + c.mq);
-  const float* p_o = p_ml + (size_t)num_seqs * num_heads * n_parts * 2;
+  const float* p_o = p_ml + partial_ml_floats(num_seqs, num_heads, n_parts);
   // each sequence's own tail: its table from entry prefix_blocks on (same row stride)
   rc = decode_core(o2, q, k_cache, v_cache, block_tables + prefix_blocks, ints + 3, num_seqs,
                    num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,

@@ -623,14 +623,22 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const AttnAr
   }
 }
 
-// Log-sum-exp merge of the partitions of one (row, query head); thread d owns
-// output dim d: M = max_p m_p, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
-// Rows with a single partition were finished by the partial kernel.  The
-// length (and the row's place in its sequence) is read first, then every
-// partition's (max, sum, o) in batches of independent loads.
+// Log-sum-exp merge of the partitions of one row: M = max_p m_p,
+// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.  Thread c of the row
+// owns 4 consecutive dims of one query head (16-byte loads of the partials;
+// the partial outputs start on a 16-byte boundary), so a 256-thread workgroup
+// covers 1,024 of the row's H*D outputs.  Rows with a single partition were
+// finished by the partial kernel.  The length (and the row's place in its
+// sequence) is read first, then every partition's (max, sum, o) in batches of
+// independent loads.
 template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(const AttnArgs a) {
-  const int hq = blockIdx.x, s = blockIdx.z, d = threadIdx.x;
+__global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
+  constexpr int kChunks = D / 4;   // 4-dim chunks per head
+  const int H = a.num_heads;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= H * kChunks) return;
+  const int hq = c / kChunks, d0 = (c % kChunks) * 4;
+  const int s = blockIdx.z;
   size_t row = s;
   int L = min(max(a.context_lens[s], 0), a.max_context_len);
   if (a.q_offsets) {  // multi-token queries: blockIdx.y = row within the sequence
@@ -642,20 +650,21 @@ __global__ __launch_bounds__(D) void merge_kernel(const AttnArgs a) {
   }
   const int n_parts = (L + a.part - 1) / a.part;
   if (n_parts <= 1) return;
-  const size_t hh = row * a.num_heads + hq;
-  typedef const __attribute__((address_space(4))) float* ConstF32Ptr;
-  const ConstF32Ptr ml = (ConstF32Ptr)(a.ws_ml + 2 * hh * a.max_parts);
-  const float* po = a.ws_o + hh * a.max_parts * D + d;
-  constexpr int kBatch = 16;
-  float M = kNegInf, num = 0.f, den = 0.f;
+  const size_t hh = row * H + hq;
+  const float* ml = a.ws_ml + 2 * hh * a.max_parts;
+  const float* po = a.ws_o + hh * a.max_parts * D + d0;
+  constexpr int kBatch = 8;
+  float M = kNegInf, den = 0.f;
+  float num[4] = {0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < n_parts; p0 += kBatch) {
-    float pm[kBatch], pl[kBatch], pv[kBatch];
+    float pm[kBatch], pl[kBatch];
+    float4 pv[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int pk = min(p0 + k, n_parts - 1);   // repeats past the end get weight 0
       pm[k] = ml[2 * pk];
       pl[k] = ml[2 * pk + 1];
-      pv[k] = po[(size_t)pk * D];
+      pv[k] = *reinterpret_cast<const float4*>(po + (size_t)pk * D);
     }
     float mx = M;
 #pragma unroll
@@ -663,29 +672,36 @@ __global__ __launch_bounds__(D) void merge_kernel(const AttnArgs a) {
       if (p0 + k < n_parts) mx = fmaxf(mx, pm[k]);
     const float ms = (mx == kNegInf) ? 0.f : mx;
     const float r = fast_exp2(M - ms);
-    num *= r;
     den *= r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[e] *= r;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const float wt = (p0 + k < n_parts) ? fast_exp2(pm[k] - ms) : 0.f;
-      num = __builtin_fmaf(wt, pv[k], num);
+      num[0] = __builtin_fmaf(wt, pv[k].x, num[0]);
+      num[1] = __builtin_fmaf(wt, pv[k].y, num[1]);
+      num[2] = __builtin_fmaf(wt, pv[k].z, num[2]);
+      num[3] = __builtin_fmaf(wt, pv[k].w, num[3]);
       den = __builtin_fmaf(wt, pl[k], den);
     }
     M = mx;
   }
-  store_out(a.out, hh * D + d, den > 0.f ? a.out_scale * num / den : 0.f, a.out_dtype);
-  if (a.lse && d == 0) a.lse[hh] = lse2_of(M, den);
+  const float inv = den > 0.f ? a.out_scale / den : 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) store_out(a.out, hh * D + d0 + e, num[e] * inv, a.out_dtype);
+  if (a.lse && d0 == 0) a.lse[hh] = lse2_of(M, den);
 }
 
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
 hipError_t launch_merge(int head_dim, int num_seqs, const AttnArgs& a, hipStream_t st) {
-  dim3 mgrid(a.num_heads, a.q_offsets ? a.max_q_len : 1, num_seqs);
+  const int chunks = a.num_heads * head_dim / 4;   // 4-dim chunks of a row
+  dim3 mgrid((chunks + 255) / 256, a.q_offsets ? a.max_q_len : 1, num_seqs);
   if (head_dim == 64)
-    hipLaunchKernelGGL((merge_kernel<64>), mgrid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((merge_kernel<64>), mgrid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((merge_kernel<128>), mgrid, dim3(128), 0, st, a);
+    hipLaunchKernelGGL((merge_kernel<128>), mgrid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -98,6 +98,19 @@ def test_multiq_many_rows_poison_and_determinism():
     assert np.array_equal(U.bits(a), U.bits(c))
 
 
+def test_multiq_odd_partial_layout():
+    """Odd rows x heads x partitions (5 x 3 x 5): the partial outputs, which the
+    kernels move as 16-byte vectors, still start on a 16-byte boundary."""
+    rng = np.random.default_rng(31)
+    st = W.allocate("odd partials", "bf16", [300], [5], 3, 1, 128, 16, rng, 31)
+    vals = W.host_values(st)
+    t = U.upload(st, vals)
+    want = U.oracle_multiq(st, vals)
+    for part in (64, 48):
+        out = U.run_multiq(st, t, out_dtype=torch.float32, partition_tokens=part)
+        U.assert_close(out, want, "bf16", f"part={part}")
+
+
 def test_multiq_with_one_row_equals_decode():
     st = W.llama3_8b_decode(3, num_seqs=6, ctx_lo=1, ctx_hi=700)
     vals = W.host_values(st)
