@@ -101,13 +101,16 @@ SplitPlan plan_split(int num_seqs, int num_kv_heads, int block_size, int max_con
 }
 
 // Split-mode workspace: int plan [2 + S + 1] (16-byte aligned), then fp32
-// (max, sum) pairs and fp32 partial outputs for (S Hk + waves) slots x G heads.
+// (max, sum) pairs padded to a multiple of 4 floats, then fp32 partial outputs
+// (16-byte aligned: the merge reads them as 16-byte vectors) for
+// (S Hk + waves) slots x G heads.
 size_t split_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                              int waves) {
   const size_t plan = ((size_t)(3 + num_seqs) * sizeof(int) + 15) / 16 * 16;
   const size_t slots = (size_t)num_seqs * num_kv_heads + waves;
   const size_t group = (size_t)(num_heads / num_kv_heads);
-  return plan + slots * group * ((size_t)head_dim + 2) * sizeof(float);
+  const size_t ml = (slots * group * 2 + 3) / 4 * 4;
+  return plan + (ml + slots * group * (size_t)head_dim) * sizeof(float);
 }
 
 void split_workspace_ptrs(void* ws, int num_seqs, int num_heads, int num_kv_heads, int waves,
@@ -117,7 +120,7 @@ void split_workspace_ptrs(void* ws, int num_seqs, int num_heads, int num_kv_head
   const size_t group = (size_t)(num_heads / num_kv_heads);
   a->plan = static_cast<int*>(ws);
   a->ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + plan);
-  a->ws_o = a->ws_ml + slots * group * 2;
+  a->ws_o = a->ws_ml + (slots * group * 2 + 3) / 4 * 4;
 }
 
 // Waves the workspace must allow for when the launch size is not known yet

@@ -463,26 +463,32 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
   }
 }
 
-// Merge of the split kernel's pieces for one (sequence, query head); thread d
-// owns output dim d.  The items of (s, g) are [a0, a0 + nb) with
-// a0 = Hk pre[s] + g nb, so the waves that covered them are a0 / chunk ..
-// (a0 + nb - 1) / chunk, and wave w left its piece in slot (s Hk + g + w) G + h.
-// Empty contexts get zero rows.  The plan, the length and the prefix sums are
-// read together, then all pieces' (max, sum, o) at once: two memory round
-// trips before the store.
+// Merge of the split kernel's pieces for one sequence; thread c owns 4
+// consecutive dims of one query head (16-byte loads of the pieces' partial
+// outputs), so a 256-thread workgroup covers 1,024 of the sequence's H*D
+// outputs.  The items of (s, g) are [a0, a0 + nb) with a0 = Hk pre[s] + g nb,
+// so the waves that covered them are a0 / chunk .. (a0 + nb - 1) / chunk, and
+// wave w left its piece in slot (s Hk + g + w) G + h.  Empty contexts get zero
+// rows.  The plan, the length and the prefix sums are read together, then the
+// pieces' (max, sum, o) in batches of independent loads.
 template <int D>
-__global__ __launch_bounds__(D) void split_merge_kernel(const AttnArgs a) {
-  const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(256) void split_merge_kernel(const AttnArgs a) {
+  constexpr int kChunks = D / 4;   // 4-dim chunks per head
   const int H = a.num_heads, Hk = a.num_kv_heads, G = a.group;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= H * kChunks) return;
+  const int hq = c / kChunks, d0 = (c % kChunks) * 4;
+  const int s = blockIdx.y;
   const int g = hq / G, h = hq - g * G;
   const ConstI32Ptr plan = as_const(a.plan);
   const int Lraw = as_const(a.context_lens)[s];
   const int chunk = plan[0];
   const int p0 = plan[2 + s], p1 = plan[3 + s];
-  const size_t oidx = ((size_t)s * H + hq) * D + d;
+  const size_t oidx = ((size_t)s * H + hq) * D + d0;
   if (min(max(Lraw, 0), a.max_context_len) == 0) {
-    store_out(a.out, oidx, 0.f, a.out_dtype);
-    if (a.lse && d == 0) a.lse[(size_t)s * H + hq] = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out(a.out, oidx + e, 0.f, a.out_dtype);
+    if (a.lse && d0 == 0) a.lse[(size_t)s * H + hq] = kNegInf;
     return;
   }
   const int nb = p1 - p0;
@@ -490,21 +496,18 @@ __global__ __launch_bounds__(D) void split_merge_kernel(const AttnArgs a) {
   const int w0 = a0 / chunk, w1 = (a0 + nb - 1) / chunk;
   if (w0 == w1) return;               // written by its one wave
   const size_t base = (size_t)s * Hk + g;
-  typedef const __attribute__((address_space(4))) float* ConstF32Ptr;
-  const ConstF32Ptr ml = (ConstF32Ptr)a.ws_ml;
-  // Pieces are folded sixteen at a time into a running log-sum-exp (M, num,
-  // den); the loads of a batch are independent.  Past the last piece the index
-  // is clamped and the weight is zero.
-  constexpr int kBatch = 16;
-  float M = kNegInf, num = 0.f, den = 0.f;
+  constexpr int kBatch = 8;
+  float M = kNegInf, den = 0.f;
+  float num[4] = {0.f, 0.f, 0.f, 0.f};
   for (int w = w0; w <= w1; w += kBatch) {
-    float pm[kBatch], pl[kBatch], po[kBatch];
+    float pm[kBatch], pl[kBatch];
+    float4 pv[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const size_t sl = (base + min(w + k, w1)) * G + h;
-      pm[k] = ml[2 * sl];
-      pl[k] = ml[2 * sl + 1];
-      po[k] = a.ws_o[sl * D + d];
+      const size_t sl = (base + min(w + k, w1)) * G + h;   // past the last piece: weight 0
+      pm[k] = a.ws_ml[2 * sl];
+      pl[k] = a.ws_ml[2 * sl + 1];
+      pv[k] = *reinterpret_cast<const float4*>(a.ws_o + sl * D + d0);
     }
     float mx = M;
 #pragma unroll
@@ -512,18 +515,24 @@ __global__ __launch_bounds__(D) void split_merge_kernel(const AttnArgs a) {
       if (w + k <= w1) mx = fmaxf(mx, pm[k]);
     const float ms = (mx == kNegInf) ? 0.f : mx;
     const float r = fast_exp2(M - ms);
-    num *= r;
     den *= r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[e] *= r;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const float wt = (w + k <= w1) ? fast_exp2(pm[k] - ms) : 0.f;
-      num = __builtin_fmaf(wt, po[k], num);
+      num[0] = __builtin_fmaf(wt, pv[k].x, num[0]);
+      num[1] = __builtin_fmaf(wt, pv[k].y, num[1]);
+      num[2] = __builtin_fmaf(wt, pv[k].z, num[2]);
+      num[3] = __builtin_fmaf(wt, pv[k].w, num[3]);
       den = __builtin_fmaf(wt, pl[k], den);
     }
     M = mx;
   }
-  store_out(a.out, oidx, den > 0.f ? a.out_scale * num / den : 0.f, a.out_dtype);
-  if (a.lse && d == 0) a.lse[(size_t)s * H + hq] = lse2_of(M, den);
+  const float inv = den > 0.f ? a.out_scale / den : 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) store_out(a.out, oidx + e, num[e] * inv, a.out_dtype);
+  if (a.lse && d0 == 0) a.lse[(size_t)s * H + hq] = lse2_of(M, den);
 }
 
 // ---------------------------------------------------------------------------
@@ -729,7 +738,9 @@ static hipError_t launch_decode_t(int num_seqs, const AttnArgs& a, hipStream_t s
     hipError_t e = launch_main(decode_split_kernel<DT, D, B, GP>, dim3(a.split_workgroups),
                                dim3(kThreads), smem, st, ev, a);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((split_merge_kernel<D>), dim3(a.num_heads, num_seqs), dim3(D), 0, st, a);
+    const int chunks = a.num_heads * D / 4;   // 4-dim chunks of a sequence's outputs
+    hipLaunchKernelGGL((split_merge_kernel<D>), dim3((chunks + 255) / 256, num_seqs), dim3(256), 0,
+                       st, a);
     return hipGetLastError();
   }
   // per-row mode launches one grid row per (sequence, query row) slot
