@@ -65,8 +65,9 @@ typedef enum {
 } pa_status;
 
 /* PA_FP8_E4M3: 8-bit floating-point codes (sign, 4 exponent bits with bias 7,
-   3 mantissa bits, no infinities; the all-ones magnitude is NaN), used only for
-   the K/V pools of paged_attn_decode_fp8kv. */
+   3 mantissa bits, no infinities; the all-ones magnitude is NaN): the K/V pools
+   of paged_attn_decode_fp8kv, and a valid dtype for the entry points that only
+   move cache bytes (paged_kv_gather, paged_kv_append, paged_kv_copy_blocks). */
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Opaque to this header; it is a hipStream_t. */

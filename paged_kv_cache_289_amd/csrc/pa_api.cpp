@@ -12,7 +12,9 @@
 namespace {
 
 bool dtype_ok(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
-int elem_bytes(int dt) { return dt == PA_F32 ? 4 : 2; }
+int elem_bytes(int dt) { return dt == PA_F32 ? 4 : dt == PA_FP8_E4M3 ? 1 : 2; }
+// the entry points that only move cache bytes also take 8-bit caches
+bool kv_dtype_ok(int dt) { return dtype_ok(dt) || dt == PA_FP8_E4M3; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -401,7 +403,7 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v
   if (num_seqs < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1 ||
       max_blocks_per_seq < 1)
     return PA_ERR_SHAPE;
-  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (!kv_dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
   if ((head_dim * elem_bytes(dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (!k_out || !v_out || !k_cache || !v_cache || !block_tables || !context_lens ||
@@ -564,7 +566,7 @@ int paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void*
     return PA_ERR_SHAPE;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
   if (total_new > 0 && num_seqs == 0) return PA_ERR_SHAPE;
-  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (!kv_dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
   if ((head_dim * elem_bytes(dtype)) % 16 != 0) return PA_ERR_UNSUPPORTED;
   // one thread per 16-byte chunk: the grid must fit a 32-bit workgroup count
   const int64_t chunks = (int64_t)total_new * num_kv_heads * (head_dim * elem_bytes(dtype) / 16);
@@ -587,7 +589,7 @@ int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
                          int dtype, pa_stream_t stream) {
   if (num_pairs < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
     return PA_ERR_SHAPE;
-  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (!kv_dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
   if (((int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype)) % 16 != 0)
     return PA_ERR_UNSUPPORTED;
   if (num_pairs == 0) return PA_OK;

@@ -101,6 +101,8 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.uint8:            # 8-bit E4M3 cache codes
+        return PA_FP8_E4M3
     try:
         return _TORCH_DT[t.dtype]
     except KeyError:

@@ -104,3 +104,33 @@ def test_full_llama3_8b_decode_fp8kv():
     want = OP.paged_decode_quant_kv(q, "bf16", k8, v8, "fp8e4m3", 0.5, 2.0, st.block_tables,
                                     st.context_lens, st.block_size, st.scale, seqs=pick)
     U.assert_close(out, want, "bf16", "llama3 8b fp8", rows=pick)
+
+
+def test_fp8_caches_through_the_byte_movers():
+    """Gather, append and block copies move 8-bit codes bit for bit."""
+    import oracle.kv_cache as OK
+    st, vals, k8, v8, t = _case(77, 128, 16, 4, S=6, ctx_lo=20, ctx_hi=200)
+    o = U.ops()
+    toff = np.concatenate([[0], np.cumsum(st.context_lens)]).astype(np.int32)
+    gk, gv = o.gather(t["k8"], t["v8"], t["block_tables"], t["context_lens"],
+                      torch.from_numpy(toff).to(U.DEV), int(toff[-1]))
+    torch.cuda.synchronize()
+    for s, (K, V) in enumerate(OP.gather_contiguous(k8, v8, st.block_tables, st.context_lens,
+                                                    st.block_size)):
+        assert np.array_equal(gk[toff[s]:toff[s + 1]].cpu().numpy(), K)
+        assert np.array_equal(gv[toff[s]:toff[s + 1]].cpu().numpy(), V)
+    rng = np.random.default_rng(3)
+    kn = rng.integers(0, 0x7E, size=(st.total_q, 2, 128), dtype=np.uint8)
+    vn = rng.integers(0, 0x7E, size=(st.total_q, 2, 128), dtype=np.uint8)
+    o.append(t["k8"], t["v8"], torch.from_numpy(kn).to(U.DEV), torch.from_numpy(vn).to(U.DEV),
+             t["block_tables"], t["context_lens"], t["q_offsets"], st.max_context_len)
+    wk, wv = OK.append_kv(k8, v8, kn, vn, st.block_tables, st.context_lens, st.q_offsets, 16)
+    torch.cuda.synchronize()
+    assert np.array_equal(t["k8"].cpu().numpy(), wk) and np.array_equal(t["v8"].cpu().numpy(), wv)
+    used = np.setdiff1d(np.unique(st.block_tables), st.free_blocks)
+    n = min(len(st.free_blocks), 4)
+    pairs = np.stack([used[:n], st.free_blocks[:n]], axis=1).astype(np.int32)
+    o.copy_blocks(t["k8"], t["v8"], torch.from_numpy(pairs).to(U.DEV))
+    ck, cv = OK.copy_blocks(wk, wv, [tuple(p) for p in pairs.tolist()])
+    torch.cuda.synchronize()
+    assert np.array_equal(t["k8"].cpu().numpy(), ck) and np.array_equal(t["v8"].cpu().numpy(), cv)
