@@ -157,31 +157,38 @@ def cpu_baseline(st, dv, budget_s, is_multiq, kv_fp8=False):
     vals = {k: W.torch_to_host(v, st.dtype) for k, v in dv.items()}
     per_tok = 2 * st.num_kv_heads * st.head_dim * (1 if kv_fp8 else st.elem_bytes)
     order = list(np.argsort(-st.context_lens))[::max(1, st.num_seqs // 16)] or [0]
+    order = list(order) + [s for s in range(st.num_seqs) if s not in order]
     done, spent, seqs_used = 0, 0.0, []
-    for s in list(order) + [s for s in range(st.num_seqs) if s not in order]:
-        if spent >= budget_s:
-            break
-        t0 = time.perf_counter()
-        if is_multiq:
-            OP.paged_multiq(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
-                            st.context_lens, st.q_offsets, st.block_size, st.scale, st.dtype,
-                            seqs=[int(s)])
-        elif kv_fp8:
-            OP.paged_decode_quant_kv(vals["q"], st.dtype, vals["k_cache"], vals["v_cache"],
-                                     "fp8e4m3", 1.0, 1.0, st.block_tables, st.context_lens,
-                                     st.block_size, st.scale, seqs=[int(s)])
-        else:
-            OP.paged_decode(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
-                            st.context_lens, st.block_size, st.scale, st.dtype, seqs=[int(s)])
-        spent += time.perf_counter() - t0
-        done += int(st.context_lens[s]) * per_tok
-        seqs_used.append(int(s))
+    passes = 0
+    # whole passes over the sequences (the first may stop early) until the time budget is spent
+    while spent < budget_s and passes < 50:
+        passes += 1
+        for s in order:
+            if spent >= budget_s:
+                break
+            t0 = time.perf_counter()
+            if is_multiq:
+                OP.paged_multiq(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
+                                st.context_lens, st.q_offsets, st.block_size, st.scale,
+                                st.dtype, seqs=[int(s)])
+            elif kv_fp8:
+                OP.paged_decode_quant_kv(vals["q"], st.dtype, vals["k_cache"], vals["v_cache"],
+                                         "fp8e4m3", 1.0, 1.0, st.block_tables, st.context_lens,
+                                         st.block_size, st.scale, seqs=[int(s)])
+            else:
+                OP.paged_decode(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
+                                st.context_lens, st.block_size, st.scale, st.dtype,
+                                seqs=[int(s)])
+            spent += time.perf_counter() - t0
+            done += int(st.context_lens[s]) * per_tok
+            seqs_used.append(int(s))
     if ctx is not None:
         ctx.unregister() if hasattr(ctx, "unregister") else None
     gbps = done / spent / 1e9 if spent > 0 else None
     return {"value": round(gbps, 4) if gbps else None, "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{len(seqs_used)} of {st.num_seqs} sequences of one layer "
+            "sample": f"{len(set(seqs_used))} of {st.num_seqs} sequences of one layer, "
+                      f"{len(seqs_used)} sequence calls over {passes} pass(es) "
                       f"({done / 2**20:.1f} MiB of KV) in {spent:.1f} s, fp64 NumPy, "
                       f"BLAS threads <= {cores}"}
 
