@@ -140,9 +140,13 @@ struct DecodeWave {
   // block past the range gets a zero-size descriptor (zeros, no memory access).
   //
   // In the last block of a sequence the slots at or beyond L may hold anything
-  // (stale or poisoned data): every lane's slot is clamped to the last valid
-  // one, so only real tokens are loaded, and the scores of the clamped
-  // duplicates are set to -inf, which gives them weight exactly 0.
+  // (stale or poisoned data): that block's descriptor ends after slot L - 1,
+  // so lanes on later slots read zeros without touching memory, and their
+  // scores are set to -inf, which gives them weight exactly 0.  Every lane's
+  // offset inside a block is therefore the same for all blocks and is
+  // computed once.  (Offsets recomputed per block would be written at the top
+  // of the ring, and the compiler may give them registers of a buffer that is
+  // still loading on some path, which makes it drain the ring there.)
   //
   // Streaming (NT) loads carry the non-temporal hint: K/V bytes that no other
   // wave reads again should not push reused lines (block tables, queries,
@@ -156,15 +160,15 @@ struct DecodeWave {
 #pragma unroll
     for (int b = 0; b < 4; ++b) colbit[b] = __builtin_amdgcn_ballot_w64((col >> b) & 1);
     uint4 kbuf[NBUF][LPB], vbuf[NBUF][LPB];
+    int voff[LPB];   // the lane's byte offsets inside a (block, KV head) slice
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) voff[i] = (i * TPL + row) * kRowBytes + col * 16;
     auto load_block = [&](int jj, int phys, bool in_range, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
-      const int last = min(B - 1, L - 1 - jj * B);   // last valid slot (wave-uniform)
-      const int nrec = in_range ? kSliceBytes : 0;
+      // the slots below L (wave-uniform; at least one for a block in range)
+      const int nrec = in_range ? min(L - jj * B, B) * kRowBytes : 0;
       const size_t boff = (size_t)phys * blk_bytes;
       const BufRsrc rk = make_rsrc(kbase + boff, nrec);
       const BufRsrc rv = make_rsrc(vbase + boff, nrec);
-      int voff[LPB];
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) voff[i] = min(i * TPL + row, last) * kRowBytes + col * 16;
       // keep the issue order K then V, and both ahead of the compute that
       // follows, so each wait covers exactly the buffer being consumed
       __builtin_amdgcn_sched_barrier(0);

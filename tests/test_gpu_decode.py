@@ -119,6 +119,26 @@ def test_decode_many_sequences(num_seqs):
         U.assert_close(out, want, "bf16", f"{num_seqs} seqs part={part}")
 
 
+@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f16", 8), ("f32", 1)])
+def test_decode_long_chunks_over_short_segments(dtype, G):
+    """Long per-wave chunks over many short contexts: one wave walks a dozen or
+    more (sequence, KV head) segments back to back, issuing each one's loads
+    while it merges and stores the one before, and leaves whole outputs and
+    pieces in the same walk; empty contexts sit in between."""
+    rng = np.random.default_rng(31 + G)
+    lens = rng.integers(0, 50, size=120)
+    lens[::11] = 0
+    st = W.allocate(f"short_{dtype}_{G}", dtype, lens, [1] * len(lens), 2 * G, 2, 128, 16, rng,
+                    13)
+    vals = W.host_values(st)
+    U.say(f"decode {dtype} G={G} 120 short contexts, sum L = {int(lens.sum())}")
+    want = U.oracle_decode(st, vals)
+    t = U.upload(st, vals)
+    for part in (16 * 7, 16 * 64):
+        out = U.run_decode(st, t, out_dtype=torch.float32, partition_tokens=part)
+        U.assert_close(out, want, dtype, f"short segments part={part}")
+
+
 def test_decode_all_contexts_empty():
     rng = np.random.default_rng(6)
     st = W.allocate("empty", "bf16", [0, 0], [1, 1], 8, 2, 128, 16, rng, 6)
