@@ -325,10 +325,6 @@ __device__ inline float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt == 0 and leaves the
-// export and LDS/scalar counters unconstrained.
-constexpr int kWaitVmcnt0 = 0x0F70;
-
 // ---------------------------------------------------------------------------
 // read-only metadata through the constant address space
 // ---------------------------------------------------------------------------

@@ -412,9 +412,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
     const int L = min(max(lens[s], 0), a.max_context_len);
     const int n_here = min(nb - j, f_end - f);
     const size_t head0 = (size_t)s * H + (size_t)g * G;
-    // drain the previous segment's stores (they share the vector-memory
-    // counter with loads) so the pipeline below starts from a known state
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     w.load_q(a.q, head0, G, a.scale_log2);
     w.reset();
     const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
