@@ -63,6 +63,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM counters) and exit")
+    ap.add_argument("--hbm-read", type=float, default=None, metavar="GIB",
+                    help="only time plain streaming reads of a GIB-GiB buffer (the device's "
+                         "HBM read ceiling, paged_hbm_read) and exit")
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 
@@ -144,53 +147,71 @@ def measured_traffic(workload: str, src_hash: str):
 # CPU baseline: the fp64 oracle on a bounded sample
 # ---------------------------------------------------------------------------
 
+def host_cores() -> int:
+    """CPU threads this process may run: its affinity set, capped by a cgroup CPU quota
+    when one is set."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, int(quota) // int(period)))
+    except (OSError, ValueError):
+        pass
+    return n
+
+
 def cpu_baseline(st, dv, budget_s, is_multiq, kv_fp8=False):
-    import torch
+    """The fp64 oracle, as it stands, on whole sequences of the same workload for about
+    ``budget_s`` seconds at one thread and again at every host core (BLAS threads set
+    with threadpoolctl); GB/s on the same KV-byte rule as the GPU figure."""
     import oracle.paged_attention as OP
     from paged_kv_cache_289_amd import workloads as W
-    try:
-        from threadpoolctl import threadpool_limits, threadpool_info
-    except ImportError:                      # pragma: no cover
-        threadpool_limits = None
-    cores = min(len(os.sched_getaffinity(0)), 16)
-    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    from threadpoolctl import threadpool_limits
     vals = {k: W.torch_to_host(v, st.dtype) for k, v in dv.items()}
     per_tok = 2 * st.num_kv_heads * st.head_dim * (1 if kv_fp8 else st.elem_bytes)
     order = list(np.argsort(-st.context_lens))[::max(1, st.num_seqs // 16)] or [0]
     order = list(order) + [s for s in range(st.num_seqs) if s not in order]
-    done, spent, seqs_used = 0, 0.0, []
-    passes = 0
-    # whole passes over the sequences (the first may stop early) until the time budget is spent
-    while spent < budget_s and passes < 50:
-        passes += 1
-        for s in order:
-            if spent >= budget_s:
-                break
-            t0 = time.perf_counter()
-            if is_multiq:
-                OP.paged_multiq(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
-                                st.context_lens, st.q_offsets, st.block_size, st.scale,
-                                st.dtype, seqs=[int(s)])
-            elif kv_fp8:
-                OP.paged_decode_quant_kv(vals["q"], st.dtype, vals["k_cache"], vals["v_cache"],
-                                         "fp8e4m3", 1.0, 1.0, st.block_tables, st.context_lens,
-                                         st.block_size, st.scale, seqs=[int(s)])
-            else:
-                OP.paged_decode(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
-                                st.context_lens, st.block_size, st.scale, st.dtype,
-                                seqs=[int(s)])
-            spent += time.perf_counter() - t0
-            done += int(st.context_lens[s]) * per_tok
-            seqs_used.append(int(s))
-    if ctx is not None:
-        ctx.unregister() if hasattr(ctx, "unregister") else None
-    gbps = done / spent / 1e9 if spent > 0 else None
-    return {"value": round(gbps, 4) if gbps else None, "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{len(set(seqs_used))} of {st.num_seqs} sequences of one layer, "
-                      f"{len(seqs_used)} sequence calls over {passes} pass(es) "
-                      f"({done / 2**20:.1f} MiB of KV) in {spent:.1f} s, fp64 NumPy, "
-                      f"BLAS threads <= {cores}"}
+
+    def one(s):
+        if is_multiq:
+            OP.paged_multiq(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
+                            st.context_lens, st.q_offsets, st.block_size, st.scale, st.dtype,
+                            seqs=[int(s)])
+        elif kv_fp8:
+            OP.paged_decode_quant_kv(vals["q"], st.dtype, vals["k_cache"], vals["v_cache"],
+                                     "fp8e4m3", 1.0, 1.0, st.block_tables, st.context_lens,
+                                     st.block_size, st.scale, seqs=[int(s)])
+        else:
+            OP.paged_decode(vals["q"], vals["k_cache"], vals["v_cache"], st.block_tables,
+                            st.context_lens, st.block_size, st.scale, st.dtype, seqs=[int(s)])
+
+    def timed(threads, budget):
+        done, spent, used, passes = 0, 0.0, [], 0
+        with threadpool_limits(limits=threads):
+            # whole passes over the sequences (the last may stop early) until the budget is spent
+            while spent < budget and passes < 50:
+                passes += 1
+                for s in order:
+                    if spent >= budget:
+                        break
+                    t0 = time.perf_counter()
+                    one(s)
+                    spent += time.perf_counter() - t0
+                    done += int(st.context_lens[s]) * per_tok
+                    used.append(int(s))
+        gbps = done / spent / 1e9 if spent > 0 else None
+        return {"value": round(gbps, 4) if gbps else None, "unit": "GB/s", "cores": threads,
+                "kind": "oracle",
+                "sample": f"{len(set(used))} of {st.num_seqs} sequences of one layer, "
+                          f"{len(used)} sequence calls over {passes} pass(es) "
+                          f"({done / 2**20:.1f} MiB of KV) in {spent:.1f} s, fp64 NumPy, "
+                          f"{threads} BLAS thread(s)"}
+
+    cores = host_cores()
+    single = timed(1, budget_s / 2)
+    res = timed(cores, budget_s / 2)
+    res["single_thread"] = {k: single[k] for k in ("value", "unit", "cores", "sample")}
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -246,13 +267,16 @@ def append_bench(a, st):
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for i in range(steps):
-        ops.LIB.paged_attn_set_kernel_events(*kev_ptrs[i])
+    for i in range(steps):        # the metric: whole calls back to back
         call(i)
     t1.record(stream)
     torch.cuda.synchronize()
-    ops.set_kernel_events(None, None)
     wall = time.perf_counter() - wall0
+    for i in range(steps):        # the roofline: each kernel between dispatch-stamped events
+        ops.LIB.paged_attn_set_kernel_events(*kev_ptrs[i])
+        call(i)
+    torch.cuda.synchronize()
+    ops.set_kernel_events(None, None)
     ms_per_step = t0.elapsed_time(t1) / steps
     kernel_ms = np.array([e0.elapsed_time(e1) for e0, e1 in kev])
     algo = 2 * new_bytes                                  # read once, written once
@@ -297,6 +321,46 @@ def append_bench(a, st):
 
 
 # ---------------------------------------------------------------------------
+# HBM read ceiling
+# ---------------------------------------------------------------------------
+
+def hbm_read_bench(a, dev):
+    """K back-to-back plain streaming reads of one buffer (cached and non-temporal
+    loads), bracketed by events: the read rate this device sustains."""
+    import torch
+    from paged_kv_cache_289_amd import ops
+    n = int(a.hbm_read * 2**30) // 16 * 16
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    buf.view(torch.int32).random_(generator=torch.Generator(device=dev).manual_seed(a.seed))
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    steps = a.steps if a.steps is not None else 20
+    warm = a.warmup if a.warmup is not None else 3
+    stream = torch.cuda.current_stream()
+    res = {"metric": "HBM streaming read GB/s (paged_hbm_read)", "unit": "GB/s", "n_gpus": 1,
+           "steps": steps, "warmup": warm, "bytes_per_read": n, "peak": PEAK_HBM_GBPS}
+    for nt in (False, True):
+        for _ in range(warm):
+            ops.hbm_read(buf, sink, nontemporal=nt, stream=stream)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(steps):
+            ops.hbm_read(buf, sink, nontemporal=nt, stream=stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        key = "nontemporal" if nt else "cached"
+        res[key] = {"ms_per_read": round(ms, 4), "GBps": round(n / (ms * 1e-3) / 1e9, 1),
+                    "frac_of_peak": round(n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    res["value"] = max(res["cached"]["GBps"], res["nontemporal"]["GBps"])
+    line = json.dumps(res)
+    print(line, flush=True)
+    if a.json_out:
+        with open(a.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+# ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
 
@@ -321,6 +385,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n}))
         return
+
+    if a.hbm_read is not None:
+        return hbm_read_bench(a, dev)
 
     is_multiq = a.workload in MULTIQ
     st = make_structure(a.workload, a.seed, a.layers, a.block_size)
@@ -414,31 +481,46 @@ def main():
           for _ in range(min(steps * calls_per_step, 64))]
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps * calls_per_step)]
-    for e0, e1 in kev:            # materialize the events before the timed region
+    for e0, e1 in kev:            # materialize the events before the timed regions
         e0.record(stream)
         e1.record(stream)
     kev_ptrs = [(ctypes.c_void_p(e0.cuda_event), ctypes.c_void_p(e1.cuda_event)) for e0, e1 in kev]
     set_events = ops.LIB.paged_attn_set_kernel_events
+
+    def pool_of(step, c):
+        return pools[(step * calls_per_step + c) % npools] if layers == 1 else pools[c]
+
+    # Timed region 1 (the metric): K whole steps back to back, with nothing
+    # between the calls.
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    k = 0
-    # the timed steps carry only the events around the main kernel (for the
-    # roofline); whole-call times are taken in a separate pass below
     for step in range(steps):
         for c in range(calls_per_step):
-            kc, vc = pools[(step * calls_per_step + c) % npools] if layers == 1 else pools[c]
-            if not a.cascade:   # (the cascade's kernels take no events: whole calls are timed)
-                set_events(*kev_ptrs[k])
-            call(kc, vc)
-            k += 1
+            call(*pool_of(step, c))
     t_end.record(stream)
     torch.cuda.synchronize()
-    ops.set_kernel_events(None, None)
-    kernel_ms = None if a.cascade else np.array([s.elapsed_time(e) for s, e in kev])
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
+
+    # Timed region 2 (the roofline): the same K steps, each call's main kernel
+    # bracketed by HIP events that the library hands to hipExtLaunchKernel on
+    # the launch stream, which stamps them with the dispatch's own start and
+    # end.  Kept out of region 1: launching through them costs a few
+    # microseconds per call.
+    kernel_ms = None
+    if not a.cascade:   # (the cascade's several kernels take no events: whole calls are timed)
+        torch.cuda.synchronize()
+        k = 0
+        for step in range(steps):
+            for c in range(calls_per_step):
+                set_events(*kev_ptrs[k])
+                call(*pool_of(step, c))
+                k += 1
+        torch.cuda.synchronize()
+        ops.set_kernel_events(None, None)
+        kernel_ms = np.array([s.elapsed_time(e) for s, e in kev])
     for k, (e0, e1) in enumerate(ev):     # informational: one call between two events
         kc, vc = pools[k % npools] if layers == 1 else pools[k % calls_per_step]
         e0.record(stream)

@@ -40,8 +40,10 @@
  *    it); out_dtype PA_F32 or equal to dtype; head_dim in {64, 128};
  *    block_size in {8, 16, 32}; num_heads % num_kv_heads == 0 with
  *    num_heads / num_kv_heads <= 16.  Anything else: PA_ERR_UNSUPPORTED.
- *  - Thread safety: reentrant; the only global state is a per-device cache of
- *    device properties.
+ *  - Thread safety: every entry point may be called from several host threads
+ *    at once.  Global state: per-device caches of device properties (filled
+ *    once, atomically), and the profiling events of
+ *    paged_attn_set_kernel_events, which are per host thread.
  */
 #ifndef PAGED_ATTN_H
 #define PAGED_ATTN_H
@@ -79,7 +81,7 @@ typedef void* pa_stream_t;
  * with the same partition_tokens (0 = the library's choice).  The workspace
  * holds the work plan and the fp32 (max, sum, unnormalized output) partials of
  * the context pieces that the log-sum-exp merge combines; its contents need no
- * initialization and are overwritten by every call (so calls that run
+ * initialization and are overwritten by every call (so calls that may run
  * concurrently need separate workspaces).  0 is a legal answer (no merge
  * needed; only for multi-token calls whose contexts fit one partition).
  * Returns 0 as well for arguments the entry points would reject.
@@ -143,7 +145,9 @@ int paged_attn_multiq(void* out, const void* q, const void* k_cache, const void*
  *   token_offsets  int32 [num_seqs + 1], device; token t of sequence s goes
  *                  to row token_offsets[s] + t; token_offsets[s+1] -
  *                  token_offsets[s] must equal context_lens[s].
- * Bytes are copied unchanged (bit-exact).
+ * Bytes are copied unchanged (bit-exact).  A table entry that is read and lies
+ * outside [0, num_blocks) is never dereferenced: the rows of its tokens are
+ * written as zeros.
  */
 int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens,
@@ -363,6 +367,19 @@ int paged_seq_blocks(const paged_block_pool* pool, int seq, int32_t* out, int ma
 int paged_seq_commit(paged_block_pool* pool, int seq, const int32_t* tokens, int num_tokens);
 int paged_seq_match_prefix(paged_block_pool* pool, int seq, const int32_t* tokens,
                            int num_tokens);
+
+/*
+ * Measurement aid, not part of the attention path: one plain streaming read of
+ * `bytes` bytes (a multiple of 16) at `buf` (16-byte aligned), 16-byte vectors
+ * in a grid-stride loop over `workgroups` workgroups of 256 threads (0 = eight
+ * per compute unit), with the non-temporal hint when `nontemporal` is nonzero.
+ * It gives the HBM read rate this device sustains, the practical ceiling to set
+ * the paged kernels' bandwidth figures against.  `sink` (one uint32, device) is
+ * written only by a data-dependent branch that keeps the loads live; its value
+ * means nothing.  Errors as for the other entry points.
+ */
+int paged_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups,
+                   int nontemporal, pa_stream_t stream);
 
 #ifdef __cplusplus
 }

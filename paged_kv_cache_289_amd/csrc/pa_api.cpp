@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "pa_internal.h"
@@ -102,27 +103,38 @@ SplitPlan plan_split(int num_seqs, int num_kv_heads, int block_size, int max_con
   return p;
 }
 
-// Split-mode workspace: int plan [2 + S + 1] (16-byte aligned), then fp32
-// (max, sum) pairs padded to a multiple of 4 floats, then fp32 partial outputs
-// (16-byte aligned: the merge reads them as 16-byte vectors) for
-// (S Hk + waves) slots x G heads.
-size_t split_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                             int waves) {
-  const size_t plan = ((size_t)(3 + num_seqs) * sizeof(int) + 15) / 16 * 16;
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Split-mode workspace, each region on a 256-byte boundary (whole cache
+// lines): the int32 plan [2 + S + 1] that the merge reads, then fp32 (max, sum)
+// pairs and fp32 partial outputs for (S Hk + waves) slots x G heads.
+struct SplitLayout {
+  size_t plan = 0, ml = 0, o = 0, total = 0;
+};
+
+SplitLayout split_layout(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int waves) {
+  SplitLayout l;
   const size_t slots = (size_t)num_seqs * num_kv_heads + waves;
   const size_t group = (size_t)(num_heads / num_kv_heads);
-  const size_t ml = (slots * group * 2 + 3) / 4 * 4;
-  return plan + (ml + slots * group * (size_t)head_dim) * sizeof(float);
+  l.plan = 0;
+  l.ml = align256((size_t)(3 + num_seqs) * sizeof(int32_t));
+  l.o = l.ml + align256(slots * group * 2 * sizeof(float));
+  l.total = l.o + slots * group * (size_t)head_dim * sizeof(float);
+  return l;
 }
 
-void split_workspace_ptrs(void* ws, int num_seqs, int num_heads, int num_kv_heads, int waves,
-                          pa::AttnArgs* a) {
-  const size_t plan = ((size_t)(3 + num_seqs) * sizeof(int) + 15) / 16 * 16;
-  const size_t slots = (size_t)num_seqs * num_kv_heads + waves;
-  const size_t group = (size_t)(num_heads / num_kv_heads);
-  a->plan = static_cast<int*>(ws);
-  a->ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + plan);
-  a->ws_o = a->ws_ml + (slots * group * 2 + 3) / 4 * 4;
+size_t split_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                             int waves) {
+  return split_layout(num_seqs, num_heads, num_kv_heads, head_dim, waves).total;
+}
+
+void split_workspace_ptrs(void* ws, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                          int waves, pa::AttnArgs* a) {
+  const SplitLayout l = split_layout(num_seqs, num_heads, num_kv_heads, head_dim, waves);
+  char* base = static_cast<char*>(ws);
+  a->plan = reinterpret_cast<int*>(base + l.plan);
+  a->ws_ml = reinterpret_cast<float*>(base + l.ml);
+  a->ws_o = reinterpret_cast<float*>(base + l.o);
 }
 
 // Waves the workspace must allow for when the launch size is not known yet
@@ -133,19 +145,20 @@ int split_waves_bound(int num_seqs, int num_kv_heads, int block_size, int max_co
                     pa::kMaxSplitWaves).waves;
 }
 
-// CUs of the current device (cached per device).
+// CUs of the current device (cached per device; threads that race on the first
+// query store the same value, atomically).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cache[dev]) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (!n) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n < 1)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 }  // namespace
@@ -276,7 +289,7 @@ int decode_core(void* out, const void* q, const void* k_cache, const void* v_cac
                                   device_cus() * wgs * pa::kWaves);
     const SplitPlan sp = plan_split(num_seqs, num_kv_heads, block_size, max_context_len,
                                     partition_tokens, resident);
-    split_workspace_ptrs(workspace, num_seqs, num_heads, num_kv_heads, sp.waves, &a);
+    split_workspace_ptrs(workspace, num_seqs, num_heads, num_kv_heads, head_dim, sp.waves, &a);
     a.chunk_blocks = sp.chunk;
     a.split_workgroups = sp.workgroups;
     a.part = 0;
@@ -308,6 +321,9 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
                       int num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
                       int dtype, int out_dtype, int partition_tokens, void* workspace,
                       size_t workspace_bytes, pa_stream_t stream) {
+  // 8-bit caches come with bf16 queries and per-tensor scales: only
+  // paged_attn_decode_fp8kv takes them (it also rejects the shapes they cannot serve)
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
   return decode_core(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                      max_context_len, scale, dtype, out_dtype, partition_tokens, workspace,
@@ -413,7 +429,7 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_cache, const void* v
     return PA_ERR_UNSUPPORTED;
   hipError_t e = pa::launch_gather(k_out, v_out, k_cache, v_cache, block_tables, context_lens,
                                     token_offsets, num_seqs, num_kv_heads, head_dim, block_size,
-                                    max_blocks_per_seq, max_blocks_per_seq, elem_bytes(dtype),
+                                    num_blocks, max_blocks_per_seq, elem_bytes(dtype),
                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -430,8 +446,6 @@ struct CascadeLayout {
   size_t ints = 0, out1 = 0, out2 = 0, lse1 = 0, lse2 = 0, mq = 0, dec = 0, total = 0;
   size_t mq_bytes = 0, dec_bytes = 0;
 };
-
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 CascadeLayout cascade_layout(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_context_len, int prefix_blocks) {
@@ -611,6 +625,18 @@ int paged_attn_check_inputs(const int32_t* block_tables, const int32_t* context_
   hipError_t e = pa::launch_check(block_tables, context_lens, num_seqs, block_size, num_blocks,
                                   max_blocks_per_seq, max_context_len, bad_count,
                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int paged_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups,
+                   int nontemporal, pa_stream_t stream) {
+  if (bytes == 0) return PA_OK;
+  if (!buf || !sink) return PA_ERR_NULL;
+  if (bytes % 16 != 0 || !aligned16(buf)) return PA_ERR_UNSUPPORTED;
+  if (workgroups < 0) return PA_ERR_SHAPE;
+  if (workgroups == 0) workgroups = device_cus() * 8;
+  hipError_t e = pa::launch_stream_read(buf, bytes, sink, workgroups, nontemporal,
+                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

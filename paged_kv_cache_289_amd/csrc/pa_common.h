@@ -3,12 +3,30 @@
 // conversions, and wave64 cross-lane reductions built on DPP.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "pa_internal.h"
 
 namespace pa {
+
+// Launch of a call's main kernel.  When profiling events are given they are
+// handed to hipExtLaunchKernel, which stamps them with the dispatch's own start
+// and end (no separate marker packets around it), so they time the kernel as
+// a kernel trace does.
+template <typename K>
+inline hipError_t launch_main(K kernel, dim3 grid, dim3 block, size_t smem, hipStream_t st,
+                              const KernelEvents& ev, const AttnArgs& a) {
+  if (ev.start || ev.stop) {
+    void* args[] = {const_cast<AttnArgs*>(&a)};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, smem, st,
+                              ev.start, ev.stop, 0);
+  }
+  hipLaunchKernelGGL(kernel, grid, block, smem, st, a);
+  return hipGetLastError();
+}
+
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -267,6 +285,18 @@ __device__ inline float row_bcast(float x, int n) {
   }
 }
 
+// Value of the lane n places further along this lane's 16-lane row, wrapping
+// (DPP row_ror; n in 1..15, a compile-time constant after unrolling).
+__device__ inline float row_ror(float x, int n) {
+  switch (n) {
+#define PA_ROW_ROR(N) \
+    case N: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+    PA_ROW_ROR(1) PA_ROW_ROR(2) PA_ROW_ROR(4) PA_ROW_ROR(8)
+#undef PA_ROW_ROR
+    default: return x;
+  }
+}
+
 // Sum over aligned groups of N lanes (N in {1,2,4,8,16,32}); every lane of a
 // group receives the group's sum.  All 64 lanes must be active.
 template <int N>
@@ -323,6 +353,21 @@ __device__ inline float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// workgroup placement
+// ---------------------------------------------------------------------------
+// The eight XCDs of the device each have their own L2, and a launch deals its
+// workgroups to them round-robin in launch order.  xcd_major(b, n) renumbers
+// the n workgroups of a 1-D launch so that consecutive numbers run on the same
+// XCD: workgroups that read the same data, given consecutive numbers, then
+// share one L2 instead of fetching that data once per XCD.  (Only a placement
+// hint: the numbering is a bijection of [0, n) whatever the hardware does.)
+constexpr int kXcds = 8;
+__device__ inline int xcd_major(int b, int n) {
+  const int x = b % kXcds, q = b / kXcds;
+  return x * (n / kXcds) + min(x, n % kXcds) + q;
 }
 
 // ---------------------------------------------------------------------------

@@ -36,6 +36,7 @@
 //    (context partition, KV head, row); its four waves interleave the
 //    partition's blocks and merge through LDS; merge_kernel combines
 //    partitions.
+#include <atomic>
 #include <type_traits>
 
 #include "pa_common.h"
@@ -76,6 +77,11 @@ struct DecodeWave {
   static constexpr bool kOwnExp = (LPT == 16);
   static constexpr int kScores = LPB * GP;
   static constexpr int kScoresPerLane = (kScores + 15) / 16;
+  // With a multiple of 16 scores, the 16 lanes of a row reduce-scatter them
+  // instead: each exchange step halves the values a lane carries, and lane c
+  // ends with exactly the sums it evaluates (scores c, c + 16, ...), with no
+  // selection afterwards.
+  static constexpr bool kScatter = kOwnExp && kScores % 16 == 0;
 
   int row, col;                 // token row within a load, 16-byte column
   typename E::QVec qv[GP];
@@ -128,6 +134,106 @@ struct DecodeWave {
     return n < kScores ? sc[n / GP][n % GP] : kNegInf;
   }
 
+  // One reduce-scatter step over the lane pairs of DPP pattern CTRL, whose two
+  // lanes differ in the bit that `mask` selects: of each pair of values (the
+  // first and second halves of x), a lane keeps the half its bit names and adds
+  // its partner's copy of that half, which the partner sends.
+  // (Plain selects, not inline asm: the compiler must see which instruction
+  // writes each value a DPP exchange reads, to keep the wait states that DPP
+  // needs after a vector write of its operand.  All selects come first, then
+  // the exchanges, so most reads sit far from their writes anyway.)
+  template <int CTRL, int N>
+  __device__ static void scatter_step(float (&x)[kScores], bool upper) {
+    float send[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) send[i] = upper ? x[i] : x[i + N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) x[i] = upper ? x[i + N / 2] : x[i];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) x[i] += dpp<CTRL>(send[i]);
+  }
+  // Partial dots of the block's scores -> in lane c (of each 16-lane row) the
+  // full scores c + 16 k, k < kScoresPerLane, in own[k].  Partners are lanes
+  // c ^ 15 (row mirror), c ^ 7 (half-row mirror), c ^ 2 and c ^ 1 (quad
+  // permutes): each keeps its partner's bits above the one it flips, so the
+  // two always hold the same set of values, and halving by bits 3, 2, 1, 0 in
+  // turn leaves lane c with entries kM c .. kM c + kM - 1 of the initial order,
+  // which therefore holds score c + 16 k at entry kM c + k.
+  __device__ void scores_scatter(const uint4 (&kr)[LPB], float (&own)[kScoresPerLane]) const {
+    constexpr int kM = kScoresPerLane;
+    float x[kScores];
+#pragma unroll
+    for (int j = 0; j < kScores; ++j) {
+      const int n = j / kM + 16 * (j % kM);   // score n: token load n / GP, head n % GP
+      x[j] = E::dot0(qv[n % GP], kr[n / GP]);
+    }
+    scatter_step<kDppRowMirror, kScores>(x, (col >> 3) & 1);
+    scatter_step<kDppRowHalfMirror, kScores / 2>(x, (col >> 2) & 1);
+    scatter_step<kDppQuadXor2, kScores / 4>(x, (col >> 1) & 1);
+    scatter_step<kDppQuadXor1, kScores / 8>(x, col & 1);
+#pragma unroll
+    for (int k = 0; k < kM; ++k) own[k] = x[k];
+  }
+
+  // One block with reduce-scattered scores: QK, the online softmax on the
+  // lane's own scores (head col % GP) and PV with the row's weights broadcast
+  // back from the lanes that evaluated them.
+  __device__ void compute_block_scatter(int jj, const uint4 (&kr)[LPB], const uint4 (&vr)[LPB],
+                                        int L, float c) {
+    constexpr int kM = kScoresPerLane;
+    float own[kM];
+    scores_scatter(kr, own);
+    if ((jj + 1) * B > L) {   // wave-uniform: only the last block of the sequence
+      asm volatile("");
+#pragma unroll
+      for (int k = 0; k < kM; ++k) {
+        const int i = (col + 16 * k) / GP;   // this score's token load
+        own[k] = (jj * B + i * TPL + row < L) ? own[k] : kNegInf;
+      }
+    }
+    // Lazy rescaling (see the header): compare the lane's scores with the
+    // running max of their head.
+    float mx = own[0];
+#pragma unroll
+    for (int k = 1; k < kM; ++k) mx = fmaxf(mx, own[k]);
+    mx *= c;
+    if (__builtin_amdgcn_ballot_w64(mx > m_lane + kRescaleLog2) != 0) {   // wave-uniform, rare
+      // the max over the row's lanes of the same head (lanes c, c + GP, ...)
+#pragma unroll
+      for (int sh = GP; sh < 16; sh *= 2) mx = fmaxf(mx, row_ror(mx, sh));
+      const float mn = fmaxf(m_lane, mx);
+      const float alpha = fast_exp2(m_lane - mn);
+      m_lane = mn;
+      l_lane *= alpha;
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {   // lane h evaluates head h
+        const float ah = row_bcast(alpha, h);
+        m[h] = row_bcast(m_lane, h);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] *= ah;
+      }
+    }
+    float pk[kM];
+#pragma unroll
+    for (int k = 0; k < kM; ++k) {
+      pk[k] = fast_exp2(__builtin_fmaf(own[k], c, -m_lane));
+      l_lane += pk[k];
+    }
+    // PV: each V element is widened once and used for all GP heads
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      float pf[GP];
+#pragma unroll
+      for (int h = 0; h < GP; ++h) pf[h] = row_bcast(pk[(i * GP + h) / 16], (i * GP + h) % 16);
+      float vf[EPL];
+      E::to_float(vr[i], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+#pragma unroll
+        for (int h = 0; h < GP; ++h) o[h][e] = __builtin_fmaf(pf[h], vf[e], o[h][e]);
+    }
+  }
+
   // Blocks j = j_begin, j_begin + step, ... < j_end of the sequence whose table
   // is tbl and whose visible length is L (j_end <= ceil(L / B)).
   //
@@ -160,15 +266,24 @@ struct DecodeWave {
 #pragma unroll
     for (int b = 0; b < 4; ++b) colbit[b] = __builtin_amdgcn_ballot_w64((col >> b) & 1);
     uint4 kbuf[NBUF][LPB], vbuf[NBUF][LPB];
-    int voff[LPB];   // the lane's byte offsets inside a (block, KV head) slice
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) voff[i] = (i * TPL + row) * kRowBytes + col * 16;
+    // The lane's byte offset inside a (block, KV head) slice for its first
+    // load; load i adds a constant, which the loads carry as their immediate
+    // offset (one offset register for all of them).
+    const int voff0 = row * kRowBytes + col * 16;
     auto load_block = [&](int jj, int phys, bool in_range, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
       // the slots below L (wave-uniform; at least one for a block in range)
       const int nrec = in_range ? min(L - jj * B, B) * kRowBytes : 0;
       const size_t boff = (size_t)phys * blk_bytes;
       const BufRsrc rk = make_rsrc(kbase + boff, nrec);
       const BufRsrc rv = make_rsrc(vbase + boff, nrec);
+      // (opaque here, so that the per-load constants below stay next to the
+      // loads and fold into their immediate offsets instead of each being
+      // hoisted into a register of its own)
+      int vo = voff0;
+      asm volatile("" : "+v"(vo));
+      int voff[LPB];
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) voff[i] = vo + i * TPL * kRowBytes;
       // keep the issue order K then V, and both ahead of the compute that
       // follows, so each wait covers exactly the buffer being consumed
       __builtin_amdgcn_sched_barrier(0);
@@ -181,6 +296,10 @@ struct DecodeWave {
     };
 
     auto compute_block = [&](int jj, const uint4 (&kr)[LPB], const uint4 (&vr)[LPB]) {
+      if constexpr (kScatter) {
+        compute_block_scatter(jj, kr, vr, L, c);
+        return;
+      }
       // QK: partial dot on the lane's 16 bytes, all-reduce over the token's lanes
       float part[LPB * GP];
 #pragma unroll
@@ -715,20 +834,21 @@ hipError_t launch_merge(int head_dim, int num_seqs, const AttnArgs& a, hipStream
   return hipGetLastError();
 }
 
-// Resident workgroups per CU of the split kernel (occupancy query, cached).
+// Resident workgroups per CU of the split kernel (occupancy query, cached;
+// threads that race on the first query store the same value, atomically).
 template <int DT, int D, int B, int GP>
 static int split_wgs_per_cu() {
-  static int cached = 0;
-  if (!cached) {
-    int n = 0;
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (!n) {
     const size_t smem = ((size_t)kMaxSplitSeqs + 1) * sizeof(int);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &n, reinterpret_cast<const void*>(decode_split_kernel<DT, D, B, GP>), kThreads,
             smem) != hipSuccess || n < 1)
       n = 1;
-    cached = n;
+    cached.store(n, std::memory_order_relaxed);
   }
-  return cached;
+  return n;
 }
 
 template <int DT, int D, int B, int GP>

@@ -12,39 +12,42 @@ namespace pa {
 
 // One workgroup per (logical block j, KV head g, sequence s); 16-byte copies.
 // Source (block phys, head g) is one contiguous B*D*elem chunk; destination
-// rows are token-major with stride Hk*D elements.
+// rows are token-major with stride Hk*D elements.  A table entry outside
+// [0, NB) is never dereferenced: its tokens' rows are written as zeros.
 __global__ __launch_bounds__(256) void gather_kernel(
     uint4* __restrict__ k_out, uint4* __restrict__ v_out, const uint4* __restrict__ kc,
     const uint4* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, const int32_t* __restrict__ tok_off, int Hk, int vec_per_row,
-    int B, int mbs) {
+    int B, int NB, int mbs) {
   const int j = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int L = min(max(lens[s], 0), mbs * B);
   const int t0 = j * B;
   if (t0 >= L) return;
   const int ntok = min(B, L - t0);
-  const size_t phys = (size_t)tables[(size_t)s * mbs + j];
-  const size_t src0 = ((phys * Hk + g) * B) * vec_per_row;
+  const int id = tables[(size_t)s * mbs + j];
+  const bool valid = id >= 0 && id < NB;
+  const size_t src0 = (((size_t)(valid ? id : 0) * Hk + g) * B) * vec_per_row;
   const size_t dst_row0 = (size_t)tok_off[s] + t0;
   for (int i = threadIdx.x; i < ntok * vec_per_row; i += blockDim.x) {
     const int r = i / vec_per_row, c = i % vec_per_row;
     const size_t dst = ((dst_row0 + r) * Hk + g) * vec_per_row + c;
-    k_out[dst] = kc[src0 + i];
-    v_out[dst] = vc[src0 + i];
+    k_out[dst] = valid ? kc[src0 + i] : make_uint4(0, 0, 0, 0);
+    v_out[dst] = valid ? vc[src0 + i] : make_uint4(0, 0, 0, 0);
   }
 }
 
 hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* context_lens,
                          const int32_t* token_offsets, int num_seqs, int num_kv_heads,
-                         int head_dim, int block_size, int max_blocks_per_seq,
-                         int max_blocks_used, int elem_bytes, hipStream_t st) {
+                         int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                         int elem_bytes, hipStream_t st) {
   const int vec_per_row = head_dim * elem_bytes / 16;
-  dim3 grid(max_blocks_used, num_kv_heads, num_seqs);
+  dim3 grid(max_blocks_per_seq, num_kv_heads, num_seqs);
   hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, st, reinterpret_cast<uint4*>(k_out),
                      reinterpret_cast<uint4*>(v_out), reinterpret_cast<const uint4*>(k_cache),
                      reinterpret_cast<const uint4*>(v_cache), block_tables, context_lens,
-                     token_offsets, num_kv_heads, vec_per_row, block_size, max_blocks_per_seq);
+                     token_offsets, num_kv_heads, vec_per_row, block_size, num_blocks,
+                     max_blocks_per_seq);
   return hipGetLastError();
 }
 

@@ -3,7 +3,6 @@
 // the hipError_t of the launch.
 #pragma once
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -74,22 +73,6 @@ struct KernelEvents {
   hipEvent_t stop = nullptr;
 };
 
-// Launch of a call's main kernel.  When profiling events are given they are
-// handed to hipExtLaunchKernel, which stamps them with the dispatch's own start
-// and end (no separate marker packets around it), so they time the kernel as
-// a kernel trace does.
-template <typename K>
-inline hipError_t launch_main(K kernel, dim3 grid, dim3 block, size_t smem, hipStream_t st,
-                              const KernelEvents& ev, const AttnArgs& a) {
-  if (ev.start || ev.stop) {
-    void* args[] = {const_cast<AttnArgs*>(&a)};
-    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, smem, st,
-                              ev.start, ev.stop, 0);
-  }
-  hipLaunchKernelGGL(kernel, grid, block, smem, st, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_decode(int dtype, int head_dim, int block_size, int group, int num_seqs,
                          const AttnArgs& a, hipStream_t stream, const KernelEvents& ev);
 
@@ -102,8 +85,8 @@ hipError_t launch_multiq(int dtype, int head_dim, int block_size, int group, int
 hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* context_lens,
                          const int32_t* token_offsets, int num_seqs, int num_kv_heads,
-                         int head_dim, int block_size, int max_blocks_per_seq,
-                         int max_blocks_used, int elem_bytes, hipStream_t stream);
+                         int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                         int elem_bytes, hipStream_t stream);
 
 hipError_t launch_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                          const int32_t* block_tables, const int32_t* context_lens,
@@ -127,6 +110,9 @@ hipError_t launch_cascade_combine(void* out, const float* ws_ml, const float* ws
                                   int n_parts, const float* o1, const float* lse1, const float* o2,
                                   const float* lse2, int num_seqs, int num_heads, int head_dim,
                                   int out_dtype, hipStream_t stream);
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int workgroups,
+                              int nontemporal, hipStream_t stream);
 
 hipError_t launch_check(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                         int block_size, int num_blocks, int max_blocks_per_seq,

@@ -13,12 +13,16 @@
 //                    holds 16 of the 32 tokens of row m = l % 32, so the row's
 //                    softmax max/sum is 16 in-lane steps plus one exchange
 //                    with lane l ^ 32 (v_permlane32_swap, no LDS).
-//   V^T = V I        the same 32x32 layout applied to V times an identity:
-//                    lane l receives V at dim 32b + l % 32 for exactly the
-//                    tokens whose probabilities it holds, in the same order.
-//   O^T += V^T P^T   A = V^T and B = P^T come straight out of those registers
-//                    (rounded to the input dtype), so nothing moves between
-//                    lanes or through LDS inside the loop.
+//   O^T += V^T P^T   B = P^T comes straight out of the score registers
+//                    (rounded to the input dtype).  A = V^T holds, in lane l,
+//                    V at dim 32b + l % 32 for exactly the tokens whose
+//                    probabilities the lane holds, in the same order (the
+//                    contraction order over a tile's tokens is free, as long
+//                    as both operands share it).  With K/V staged in LDS
+//                    (rows layout below) two LDS transpose reads
+//                    (ds_read_b64_tr_b16) give it per 16-token step; with
+//                    K/V loaded straight into registers (token layout) an
+//                    MFMA of V with an identity puts V into that layout.
 //
 // The four waves of a workgroup split the partition's tiles, each keeping its
 // next tile's loads in flight while it computes one; their (max, sum, O)
@@ -107,18 +111,32 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
   constexpr int DB = D / 32;   // 32-dim blocks of the output
   constexpr int kElem = 2;
   constexpr int kRowBytes = D * kElem;
-  constexpr int RS = kRowBytes + 16;       // LDS row stride in bytes
-  constexpr int kTileBytes = 32 * RS;      // one K or V tile in LDS
+  // LDS row strides.  K rows are read 16 bytes per lane, 16 rows per pass:
+  // 16 bytes of padding (4 dwords) spread those rows over all banks.  V rows
+  // are read by transpose reads, 4 rows x 64 bytes per half-wave: 64 bytes of
+  // padding (16 dwords, so 16 or 48 dwords modulo the 64 banks) keeps those
+  // four rows in disjoint banks.
+  constexpr int RS = kRowBytes + 16;       // K
+  constexpr int RSV = kRowBytes + 64;      // V
+  constexpr int kTileBytes = 32 * RS;      // one K tile in LDS
+  constexpr int kStageBytes = kTileBytes + 32 * RSV;   // a K tile and a V tile
   constexpr int CPR = kRowBytes / 16;      // 16-byte chunks per token row
   constexpr int NP = ROWS ? kThreads : 64; // threads staging one tile
   constexpr int kPer = 32 * CPR / NP;      // chunks per staging thread per tensor
   static_assert(kPer * NP == 32 * CPR && NP % CPR == 0, "staging layout");
 
   const int G = a.group, H = a.num_heads, Hk = a.num_kv_heads;
-  const int g = blockIdx.y, s = blockIdx.z;
   const int rt_count = (a.max_q_len * G + 31) / 32;
   const int units = ROWS ? (rt_count + kWaves - 1) / kWaves : rt_count;
-  const int ux = blockIdx.x % units, p = blockIdx.x / units;
+  // One workgroup per (row unit, partition, KV head, sequence), numbered so
+  // that the row units of one (partition, KV head, sequence), which read the
+  // same K/V tiles, run on one XCD.
+  int wg = xcd_major(blockIdx.x, gridDim.x);
+  const int ux = wg % units;
+  wg /= units;
+  const int p = wg % a.max_parts;
+  wg /= a.max_parts;
+  const int g = wg % Hk, s = wg / Hk;
   const int q0 = a.q_offsets[s], n = a.q_offsets[s + 1] - q0;
   const int n_rows = n * G;
   const int wg_row0 = (ROWS ? ux * kWaves : ux) * 32;
@@ -228,7 +246,7 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
       sv[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
     }
   };
-  constexpr int kLdsBytes = ROWS ? 2 * 2 * kTileBytes : 16;   // (only the rows layout stages)
+  constexpr int kLdsBytes = ROWS ? 2 * kStageBytes : 16;   // (only the rows layout stages)
   __shared__ __attribute__((aligned(16))) char sm_kv[kLdsBytes];
   // base: K tile, base + kTileBytes: V tile
   auto stage_store = [&](char* base, const u32x4_t (&sk)[kPer], const u32x4_t (&sv)[kPer]) {
@@ -236,20 +254,42 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
     for (int i = 0; i < kPer; ++i) {
       const int tok = spid / CPR + i * (NP / CPR);
       *reinterpret_cast<u32x4_t*>(base + tok * RS + scol * 16) = sk[i];
-      *reinterpret_cast<u32x4_t*>(base + kTileBytes + tok * RS + scol * 16) = sv[i];
+      *reinterpret_cast<u32x4_t*>(base + kTileBytes + tok * RSV + scol * 16) = sv[i];
     }
   };
-  // this lane's operands: token mcol, dims 16 ks + 8 hh .. +7
-  auto lds_read = [&](const char* base, uint4 (&kr)[KS], uint4 (&vr)[KS]) {
+  // this lane's K operands: token mcol, dims 16 ks + 8 hh .. +7
+  auto lds_read_k = [&](const char* base, uint4 (&kr)[KS]) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       kr[ks] = *reinterpret_cast<const uint4*>(base + mcol * RS + 32 * ks + 16 * hh);
+  };
+  // this lane's V^T operands for dim block db and 16-token step ks: dim
+  // 32 db + mcol, tokens 16 ks + 4 hh + (0..3) then 16 ks + 8 + 4 hh + (0..3),
+  // the order of its probabilities.  In a transpose read, lane i of each
+  // 16-lane group addresses row r0 + i / 4 at dims c0 + 4 (i % 4) .. + 3, and
+  // lane j receives dim c0 + j of rows r0 .. r0 + 3.
+  auto lds_read_vt = [&](const char* base, uint4 (&va)[DB][2]) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 LdsV4;
+    const int trow = 4 * hh + (lane & 15) / 4;
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      vr[ks] = *reinterpret_cast<const uint4*>(base + kTileBytes + mcol * RS + 32 * ks + 16 * hh);
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const char* p0 = base + kTileBytes + (16 * ks + trow) * RSV + (32 * db + tcol) * 2;
+        const auto lo = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                      (LdsV4*)(__attribute__((address_space(3))) char*)p0));
+        const auto hi = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                      (LdsV4*)(__attribute__((address_space(3))) char*)(p0 + 8 * RSV)));
+        va[db][ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
   };
 
-  auto compute_tile = [&](int t0, const uint4 (&kr)[KS], const uint4 (&vr)[KS]) {
+  // QK^T, masking and the online softmax of one tile; returns the P^T operands
+  // (pb: p rounded or cut to the input dtype, pl: bf16 residual)
+  auto softmax_tile = [&](int t0, const uint4 (&kr)[KS], uint4& pb0, uint4& pb1, uint4& pl0,
+                          uint4& pl1) {
     // S^T = K Q^T: lane holds tokens t0 + tile_token(v, hh) of its row
     f32x16_t sc = f32x16_t{};
 #pragma unroll
@@ -291,7 +331,6 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
     // low 16 bits cleared, exact) and the residual p - head (exact in fp32,
     // then rounded to bf16), and both are multiplied: p is carried to about
     // 2^-16.  f16's 11 bits are used as they are (rounded to nearest).
-    uint4 pb0, pb1, pl0, pl1;
     if constexpr (DT == PA_BF16) {
       f32x16_t res;
 #pragma unroll
@@ -305,18 +344,27 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
       pb0 = pack8<DT>(sc, 0);
       pb1 = pack8<DT>(sc, 8);
     }
+  };
+  // O^T += V^T P^T for dim block db from its two 16-token V^T operands
+  auto pv_block = [&](int db, const uint4& va0, const uint4& va1, const uint4& pb0,
+                      const uint4& pb1, const uint4& pl0, const uint4& pl1) {
+    o[db] = M::mma(va0, pb0, o[db]);
+    o[db] = M::mma(va1, pb1, o[db]);
+    if constexpr (DT == PA_BF16) {
+      o[db] = M::mma(va0, pl0, o[db]);
+      o[db] = M::mma(va1, pl1, o[db]);
+    }
+  };
+  // token layout: V rows in registers (token mcol) -> V^T through the identity
+  auto compute_tile = [&](int t0, const uint4 (&kr)[KS], const uint4 (&vr)[KS]) {
+    uint4 pb0, pb1, pl0, pl1;
+    softmax_tile(t0, kr, pb0, pb1, pl0, pl1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       // V I reproduces the V values exactly, so repacking them is exact
       f32x16_t vt = M::mma(vr[2 * db], eye[0], f32x16_t{});
       vt = M::mma(vr[2 * db + 1], eye[1], vt);
-      const uint4 va0 = pack8_exact<DT>(vt, 0), va1 = pack8_exact<DT>(vt, 8);
-      o[db] = M::mma(va0, pb0, o[db]);
-      o[db] = M::mma(va1, pb1, o[db]);
-      if constexpr (DT == PA_BF16) {
-        o[db] = M::mma(va0, pl0, o[db]);
-        o[db] = M::mma(va1, pl1, o[db]);
-      }
+      pv_block(db, pack8_exact<DT>(vt, 0), pack8_exact<DT>(vt, 8), pb0, pb1, pl0, pl1);
     }
   };
 
@@ -329,9 +377,13 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
     // is unconditional.
     auto compute_from = [&](int t0, const char* base) {
       if (t0 < tok_end) {   // wave-uniform: the wave's rows see keys in this tile
-        uint4 kr[KS], vr[KS];
-        lds_read(base, kr, vr);
-        compute_tile(t0, kr, vr);
+        uint4 kr[KS], va[DB][2];
+        lds_read_k(base, kr);
+        lds_read_vt(base, va);
+        uint4 pb0, pb1, pl0, pl1;
+        softmax_tile(t0, kr, pb0, pb1, pl0, pl1);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) pv_block(db, va[db][0], va[db][1], pb0, pb1, pl0, pl1);
       }
     };
     int t0 = tok0;
@@ -343,13 +395,13 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
     while (t0 + 32 < wg_end) {
       stage_load(t0 + 32, sk, sv);
       __builtin_amdgcn_sched_barrier(0);
-      compute_from(t0, sm_kv + buf * 2 * kTileBytes);
+      compute_from(t0, sm_kv + buf * kStageBytes);
       buf ^= 1;
-      stage_store(sm_kv + buf * 2 * kTileBytes, sk, sv);
+      stage_store(sm_kv + buf * kStageBytes, sk, sv);
       __syncthreads();
       t0 += 32;
     }
-    compute_from(t0, sm_kv + buf * 2 * kTileBytes);
+    compute_from(t0, sm_kv + buf * kStageBytes);
   } else {
     // Each wave takes tiles tok0 + 32 wave, + 32 kWaves, ... and loads them
     // straight into registers in the operand layout (lane (mcol, hh) reads
@@ -482,7 +534,7 @@ static hipError_t launch_mfma_t(int num_seqs, const AttnArgs& a, hipStream_t st,
   const int rt_count = (a.max_q_len * a.group + 31) / 32;
   const bool rows = multiq_rows_mode(a.max_q_len, a.group);
   const int units = rows ? (rt_count + kWaves - 1) / kWaves : rt_count;
-  dim3 grid(units * a.max_parts, a.num_kv_heads, num_seqs);
+  dim3 grid(units * a.max_parts * a.num_kv_heads * num_seqs);
   const hipError_t e =
       rows ? launch_main(multiq_mfma_rows_kernel<DT, D, B>, grid, dim3(kThreads), 0, st, ev, a)
            : launch_main(multiq_mfma_kernel<DT, D, B>, grid, dim3(kThreads), 0, st, ev, a);

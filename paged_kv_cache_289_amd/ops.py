@@ -8,13 +8,17 @@ this module raises if the library has not been built
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+# PAGED_ATTN_LIB names another build of the same library (e.g. a host-side
+# sanitizer build for the CPU tests); the in-tree build is the default.
+_LIB_PATH = os.environ.get("PAGED_ATTN_LIB") or \
+    os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = \
     0, -1, -2, -3, -4, -5
@@ -43,6 +47,7 @@ SIGNATURES = {
                                      _F, _F, _I, _I, _P, _Z, _P]),
     "paged_kv_append": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "paged_kv_copy_blocks": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "paged_hbm_read": (_I, [_P, _Z, _P, _I, _I, _P]),
     "paged_pool_create": (_P, [_I, _I]),
     "paged_pool_destroy": (None, [_P]),
     "paged_pool_num_free": (_I, [_P]),
@@ -115,6 +120,15 @@ def _need_contig(**ts):
             raise PagedAttnError(n, PA_ERR_SHAPE, f"{n} must be contiguous")
 
 
+def _same_dtype(q, k_cache, v_cache):
+    """The attention entry points read K/V in the query's type (8-bit caches go through
+    :func:`decode_fp8kv`); a mismatch would make the kernels mis-size every row."""
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise PagedAttnError("dtype", PA_ERR_UNSUPPORTED,
+                             f"K/V caches ({k_cache.dtype}, {v_cache.dtype}) must have the "
+                             f"query's dtype {q.dtype}")
+
+
 def default_partition(num_seqs, num_heads, num_kv_heads, block_size, max_context_len,
                       max_q_len=1) -> int:
     return LIB.paged_attn_default_partition(num_seqs, num_heads, num_kv_heads, block_size,
@@ -128,12 +142,33 @@ def workspace_size(num_seqs, total_q, max_q_len, num_heads, num_kv_heads, head_d
                                              max_context_len, partition_tokens))
 
 
-def _workspace(nbytes: int, device, workspace):
+def _alloc_stream(stream):
+    """The torch stream the library will launch on, as a context for allocating the
+    call's temporaries: the caching allocator then hands their memory to later
+    allocations only in that stream's order, never while the kernels may still use it.
+    A null context when the call runs on the current stream."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream.cuda_stream) if hasattr(stream, "cuda_stream")
+                                           else int(stream))
+    if stream == torch.cuda.current_stream():
+        return contextlib.nullcontext()
+    return torch.cuda.stream(stream)
+
+
+def _empty(shape, dtype, device, stream):
+    with _alloc_stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _workspace(nbytes: int, device, workspace, stream=None):
     if nbytes == 0:
         return workspace, (workspace.numel() * workspace.element_size() if workspace is not None
                            else 0)
     if workspace is None:
-        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        with _alloc_stream(stream):
+            workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -151,11 +186,12 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     S, H, D = q.shape
     NB, Hk, B, D2 = k_cache.shape
     assert D2 == D and v_cache.shape == k_cache.shape and block_tables.shape[0] == S
+    _same_dtype(q, k_cache, v_cache)
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
     if out is None:
-        out = torch.empty((S, H, D), dtype=out_dtype or q.dtype, device=q.device)
+        out = _empty((S, H, D), out_dtype or q.dtype, q.device, stream)
     need = workspace_size(S, S, 1, H, Hk, D, B, max_context_len, partition_tokens)
-    workspace, wbytes = _workspace(need, q.device, workspace)
+    workspace, wbytes = _workspace(need, q.device, workspace, stream)
     rc = LIB.paged_attn_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                _ptr(block_tables), _ptr(context_lens), S, H, Hk, D, B, NB,
                                block_tables.shape[1], int(max_context_len), float(scale),
@@ -178,10 +214,11 @@ def multiq(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     NB, Hk, B, _ = k_cache.shape
     S = context_lens.shape[0]
     assert q_offsets.shape[0] == S + 1 and q_offsets.dtype == torch.int32
+    _same_dtype(q, k_cache, v_cache)
     if out is None:
-        out = torch.empty((T, H, D), dtype=out_dtype or q.dtype, device=q.device)
+        out = _empty((T, H, D), out_dtype or q.dtype, q.device, stream)
     need = workspace_size(S, T, max_q_len, H, Hk, D, B, max_context_len, partition_tokens)
-    workspace, wbytes = _workspace(need, q.device, workspace)
+    workspace, wbytes = _workspace(need, q.device, workspace, stream)
     rc = LIB.paged_attn_multiq(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                _ptr(block_tables), _ptr(context_lens), _ptr(q_offsets), S, T,
                                int(max_q_len), H, Hk, D, B, NB, block_tables.shape[1],
@@ -203,8 +240,9 @@ def _shared_prefix_args(q, k_cache, v_cache, block_tables, context_lens, scale, 
                         prefix_blocks, out, workspace, stream):
     S, H, D = q.shape
     NB, Hk, B, _ = k_cache.shape
+    _same_dtype(q, k_cache, v_cache)
     need = shared_prefix_workspace_size(S, H, Hk, D, B, max_context_len, prefix_blocks)
-    workspace, wbytes = _workspace(need, q.device, workspace)
+    workspace, wbytes = _workspace(need, q.device, workspace, stream)
     args = [_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
             _ptr(context_lens), S, H, Hk, D, B, NB, block_tables.shape[1], int(max_context_len),
             int(prefix_blocks), ctypes.c_float(scale), _dtype(q), _dtype(out), _ptr(workspace),
@@ -222,7 +260,7 @@ def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
                  context_lens=context_lens, out=out)
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+        out = _empty(q.shape, out_dtype or q.dtype, q.device, stream)
     args, workspace = _shared_prefix_args(q, k_cache, v_cache, block_tables, context_lens, scale,
                                           max_context_len, prefix_blocks, out, workspace, stream)
     _check("paged_attn_decode_shared_prefix", LIB.paged_attn_decode_shared_prefix(*args))
@@ -247,7 +285,7 @@ def _fp8kv_args(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
     S, H, D = q.shape
     NB, Hk, B, _ = k_cache.shape
     need = workspace_size(S, S, 1, H, Hk, D, B, max_context_len, partition_tokens)
-    workspace, wbytes = _workspace(need, q.device, workspace)
+    workspace, wbytes = _workspace(need, q.device, workspace, stream)
     args = [_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
             _ptr(context_lens), S, H, Hk, D, B, NB, block_tables.shape[1], int(max_context_len),
             ctypes.c_float(scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale), _dtype(out),
@@ -265,7 +303,7 @@ def decode_fp8kv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
                  context_lens=context_lens, out=out)
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+        out = _empty(q.shape, out_dtype or q.dtype, q.device, stream)
     args, workspace = _fp8kv_args(q, k_cache, v_cache, block_tables, context_lens, scale,
                                   k_scale, v_scale, max_context_len, out, workspace, stream,
                                   partition_tokens)
@@ -293,8 +331,8 @@ def gather(k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Ten
                  context_lens=context_lens, token_offsets=token_offsets)
     NB, Hk, B, D = k_cache.shape
     S = context_lens.shape[0]
-    k_out = torch.empty((total_tokens, Hk, D), dtype=k_cache.dtype, device=k_cache.device)
-    v_out = torch.empty_like(k_out)
+    k_out = _empty((total_tokens, Hk, D), k_cache.dtype, k_cache.device, stream)
+    v_out = _empty((total_tokens, Hk, D), k_cache.dtype, k_cache.device, stream)
     rc = LIB.paged_kv_gather(_ptr(k_out), _ptr(v_out), _ptr(k_cache), _ptr(v_cache),
                              _ptr(block_tables), _ptr(context_lens), _ptr(token_offsets), S, Hk,
                              D, B, NB, block_tables.shape[1], _dtype(k_cache), _stream(stream))
@@ -331,8 +369,9 @@ def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_c
                  context_lens=context_lens, out=out)
     S, H, D = q.shape
     NB, Hk, B, _ = k_cache.shape
+    _same_dtype(q, k_cache, v_cache)
     need = workspace_size(S, S, 1, H, Hk, D, B, max_context_len, partition_tokens)
-    workspace, wbytes = _workspace(need, q.device, workspace)
+    workspace, wbytes = _workspace(need, q.device, workspace, stream)
     args = [_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
             _ptr(context_lens), S, H, Hk, D, B, NB, block_tables.shape[1], int(max_context_len),
             ctypes.c_float(scale), _dtype(q), _dtype(out), int(partition_tokens),
@@ -350,8 +389,9 @@ def prepare_multiq(q, k_cache, v_cache, block_tables, context_lens, q_offsets, s
     T, H, D = q.shape
     NB, Hk, B, _ = k_cache.shape
     S = context_lens.shape[0]
+    _same_dtype(q, k_cache, v_cache)
     need = workspace_size(S, T, max_q_len, H, Hk, D, B, max_context_len, partition_tokens)
-    workspace, wbytes = _workspace(need, q.device, workspace)
+    workspace, wbytes = _workspace(need, q.device, workspace, stream)
     args = [_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
             _ptr(context_lens), _ptr(q_offsets), S, T, int(max_q_len), H, Hk, D, B, NB,
             block_tables.shape[1], int(max_context_len), ctypes.c_float(scale),
@@ -379,7 +419,7 @@ def set_kernel_events(start=None, stop=None):
 def check_inputs(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int,
                  num_blocks: int, max_context_len: int, stream=None) -> torch.Tensor:
     """Device int32 scalar: count of bad context lengths and out-of-range block ids."""
-    bad = torch.empty((1,), dtype=torch.int32, device=block_tables.device)
+    bad = _empty((1,), torch.int32, block_tables.device, stream)
     S, mbs = block_tables.shape
     rc = LIB.paged_attn_check_inputs(_ptr(block_tables), _ptr(context_lens), S, block_size,
                                      num_blocks, mbs, max_context_len, _ptr(bad), _stream(stream))
@@ -488,3 +528,13 @@ class BlockPool:
         buf = (ctypes.c_int32 * max(len(tokens), 1))(*tokens)
         return self._ok("paged_seq_match_prefix",
                         LIB.paged_seq_match_prefix(self._h, int(seq), buf, len(tokens)))
+
+
+def hbm_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, nontemporal: bool = False,
+             stream=None):
+    """One streaming read of all of ``buf`` (a measurement aid: the device's HBM read rate)."""
+    _need_contig(buf=buf)
+    rc = LIB.paged_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                            int(workgroups), 1 if nontemporal else 0, _stream(stream))
+    _check("paged_hbm_read", rc)
+

@@ -84,13 +84,22 @@ def oracle_multiq(st, vals, causal=True, seqs=None):
                            causal=causal, seqs=seqs)
 
 
-def run_decode(st, t, out_dtype=None, partition_tokens=0):
+def run_decode(st, t, out_dtype=None, partition_tokens=0, workspace=None):
     o = ops()
     out = o.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
                    st.scale, st.max_context_len, out_dtype=out_dtype,
-                   partition_tokens=partition_tokens)
+                   partition_tokens=partition_tokens, workspace=workspace)
     torch.cuda.synchronize()
     return out
+
+
+def assert_rounds(low: torch.Tensor, f32: torch.Tensor, label: str):
+    """A bf16/fp16 output is the round-to-nearest-even of the same call's fp32
+    output, bit for bit: the kernel's own error is the fp32 output's (held to the
+    strict bar), and the narrow output adds only its rounding."""
+    want = f32.to(low.dtype)
+    eq = bits(low) == bits(want)
+    assert eq.all(), f"{label}: {int((~eq).sum())} outputs differ from the rounded fp32 result"
 
 
 def run_multiq(st, t, causal=True, out_dtype=None, partition_tokens=0):

@@ -72,6 +72,30 @@ def test_decode_rejects_bad_arguments_on_host(kw, code):
     assert _decode(**kw) == code
 
 
+@pytest.mark.parametrize("kw", [dict(dt=3), dict(dt=3, D=64, B=8), dict(dt=3, H=64, Hk=4),
+                                dict(dt=3, odt=ops.PA_F32)])
+def test_plain_decode_rejects_8bit_caches(kw):
+    # 8-bit E4M3 caches (code 3) are served by paged_attn_decode_fp8kv only, which
+    # also rejects the shapes the 8-bit kernels cannot take
+    assert ops.PA_FP8_E4M3 == 3
+    assert _decode(**kw) == ops.PA_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_cache_dtype_other_than_the_query():
+    import torch
+    q = torch.zeros((2, 8, 128), dtype=torch.bfloat16)
+    codes = torch.zeros((4, 2, 16, 128), dtype=torch.uint8)
+    tbl = torch.zeros((2, 4), dtype=torch.int32)
+    lens = torch.ones((2,), dtype=torch.int32)
+    qoff = torch.tensor([0, 1, 2], dtype=torch.int32)
+    with pytest.raises(ops.PagedAttnError) as e:
+        ops.decode(q, codes, codes, tbl, lens, 0.1, 16)
+    assert e.value.status == ops.PA_ERR_UNSUPPORTED
+    with pytest.raises(ops.PagedAttnError):
+        ops.multiq(q, codes.view(torch.float16), codes.view(torch.float16), tbl, lens, qoff, 0.1,
+                   16, 1)
+
+
 def test_decode_with_no_sequences_is_a_no_op():
     assert _decode(S=0, q=None, out=None) == ops.PA_OK
 
@@ -111,10 +135,12 @@ def test_gather_and_check_reject_bad_arguments_on_host():
 def test_workspace_size_formula():
     # Decode, 64 sequences x 8 KV heads (G = 4), head_dim 128, contexts up to 4096 in
     # 16-token blocks, 256-token pieces: at most 64*8*256 = 131072 items in pieces of 16
-    # blocks -> 8192 waves; the plan (2 + 65 ints, 16-byte rounded) then fp32 (max, sum)
-    # and outputs for (64*8 + 8192) slots x 4 heads.
+    # blocks -> 8192 waves; the plan (2 + 65 int32, on 256 bytes), then fp32 (max, sum)
+    # and outputs for (64*8 + 8192) slots x 4 heads, each region on a 256-byte boundary.
     n = ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 256)
-    assert n == 272 + (64 * 8 + 8192) * 4 * 130 * 4
+    slots = 64 * 8 + 8192
+    assert n == 512 + slots * 4 * 2 * 4 + slots * 4 * 128 * 4
+    assert (slots * 4 * 2 * 4) % 256 == 0
     # default pieces: the launch never exceeds 8192 waves
     assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 0) == n
     # multi-token rows whose contexts fit one partition need no workspace

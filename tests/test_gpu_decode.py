@@ -51,6 +51,35 @@ def test_gather_is_bit_exact(case):
     assert np.array_equal(W.torch_to_host(vo, st.dtype), vref)
 
 
+def test_gather_out_of_range_ids_give_zero_rows():
+    """Table entries outside [0, num_blocks) are never dereferenced: the tokens of
+    those blocks come out as zero rows, every other row as the oracle's gather."""
+    st = W.llama3_8b_decode(2, num_seqs=4, ctx_lo=40, ctx_hi=120)
+    vals = W.host_values(st)
+    tbl = st.block_tables.copy()
+    tbl[1, 0] = st.num_blocks
+    tbl[2, 1] = -3
+    t = U.upload(st, vals)
+    tok_off = np.zeros(st.num_seqs + 1, np.int32)
+    np.cumsum(st.context_lens, out=tok_off[1:])
+    ko, vo = U.ops().gather(t["k_cache"], t["v_cache"], torch.from_numpy(tbl).to(U.DEV),
+                            t["context_lens"], torch.from_numpy(tok_off).to(U.DEV),
+                            int(tok_off[-1]))
+    torch.cuda.synchronize()
+    ref = OP.gather_contiguous(vals["k_cache"], vals["v_cache"], st.block_tables,
+                               st.context_lens, st.block_size)
+    kref = np.concatenate([k for k, _ in ref])
+    vref = np.concatenate([v for _, v in ref])
+    B = st.block_size
+    for s, j in ((1, 0), (2, 1)):
+        lo = tok_off[s] + j * B
+        hi = min(tok_off[s] + (j + 1) * B, tok_off[s + 1])
+        kref[lo:hi] = 0
+        vref[lo:hi] = 0
+    assert np.array_equal(W.torch_to_host(ko, st.dtype), kref)
+    assert np.array_equal(W.torch_to_host(vo, st.dtype), vref)
+
+
 # --------------------------------------------------------------------------
 # small cases: the whole oracle
 # --------------------------------------------------------------------------
@@ -76,9 +105,12 @@ def test_decode_shapes(dtype, D, B, G):
     t = U.upload(st, vals)
     want = U.oracle_decode(st, vals)
     for part in (0, 4 * B):
-        for odt in (None, torch.float32):
-            out = U.run_decode(st, t, out_dtype=odt, partition_tokens=part)
-            U.assert_close(out, want, dtype, f"part={part} out={out.dtype}")
+        out32 = U.run_decode(st, t, out_dtype=torch.float32, partition_tokens=part)
+        U.assert_close(out32, want, dtype, f"part={part} out=f32")
+        out = U.run_decode(st, t, partition_tokens=part)
+        U.assert_close(out, want, dtype, f"part={part} out={out.dtype}")
+        if dtype != "f32":
+            U.assert_rounds(out, out32, f"part={part}")
 
 
 def test_decode_non_power_of_two_group():
@@ -137,6 +169,27 @@ def test_decode_long_chunks_over_short_segments(dtype, G):
     for part in (16 * 7, 16 * 64):
         out = U.run_decode(st, t, out_dtype=torch.float32, partition_tokens=part)
         U.assert_close(out, want, dtype, f"short segments part={part}")
+
+
+def test_decode_reuses_one_workspace():
+    """One workspace, filled with garbage first, serves calls of different shapes and
+    piece sizes in turn (nothing in it needs initializing, and nothing left by an
+    earlier call leaks into a later one): each result equals the same call on a fresh
+    workspace bit for bit, and the oracle."""
+    o = U.ops()
+    cases = [(_small_bf16(51), 64), (_small_bf16(52, num_seqs=9, ctx_hi=900), 32),
+             (_small_bf16(53, num_seqs=4), 0), (_small_bf16(51), 16), (_small_bf16(54), 0)]
+    need = max(o.workspace_size(st.num_seqs, st.num_seqs, 1, st.num_heads, st.num_kv_heads,
+                                st.head_dim, st.block_size, st.max_context_len, part)
+               for st, part in cases)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=U.DEV)
+    for st, part in cases:
+        vals = W.host_values(st)
+        t = U.upload(st, vals)
+        a = U.run_decode(st, t, out_dtype=torch.float32, partition_tokens=part, workspace=ws)
+        b = U.run_decode(st, t, out_dtype=torch.float32, partition_tokens=part)
+        assert np.array_equal(U.bits(a), U.bits(b)), f"S={st.num_seqs} part={part}"
+        U.assert_close(a, U.oracle_decode(st, vals), "bf16", f"reused S={st.num_seqs} part={part}")
 
 
 def test_decode_all_contexts_empty():
@@ -242,31 +295,51 @@ def _sample(st, k, seed):
     return sorted(pick)
 
 
-def _full_size(st, k_seqs, seed):
-    U.say(f"full size {st.name}: {st.summary()}")
-    dv = W.device_values(st, U.DEV)
-    t = dict(dv)
-    t["block_tables"] = torch.from_numpy(st.block_tables).to(U.DEV)
-    t["context_lens"] = torch.from_numpy(st.context_lens).to(U.DEV)
-    out = U.run_decode(st, t)
-    out32 = U.run_decode(st, t, out_dtype=torch.float32)
-    seqs = _sample(st, k_seqs, seed)
-    vals = {k: W.torch_to_host(v, st.dtype) for k, v in dv.items()}
-    want = U.oracle_decode(st, vals, seqs=seqs)
-    U.assert_close(out32, want, st.dtype, f"{st.name} out f32", rows=seqs)
-    U.assert_close(out, want, st.dtype, f"{st.name} out {st.dtype}", rows=seqs)
+def _full_size(st, layers=(0,)):
+    """The benchmark's inputs (device-generated; for a multi-layer pool the queries of
+    layer 0 and the K/V pool of each listed layer, as the benchmark pairs them), its
+    launch configuration and workspace reuse; every sequence is compared with the
+    oracle, one at a time."""
+    U.say(f"full size {st.name}: {st.summary()} layers {list(layers)}")
+    q = W.device_values(st, U.DEV)["q"]
+    tbl = torch.from_numpy(st.block_tables).to(U.DEV)
+    lens = torch.from_numpy(st.context_lens).to(U.DEV)
+    o = U.ops()
+    ws = torch.zeros(o.workspace_size(st.num_seqs, st.num_seqs, 1, st.num_heads,
+                                      st.num_kv_heads, st.head_dim, st.block_size,
+                                      st.max_context_len), dtype=torch.uint8, device=U.DEV)
+    qh = W.torch_to_host(q, st.dtype)
+    for layer in layers:
+        dv = W.device_values(st, U.DEV, layer=layer)
+        t = {"q": q, "k_cache": dv["k_cache"], "v_cache": dv["v_cache"], "block_tables": tbl,
+             "context_lens": lens}
+        out = U.run_decode(st, t, workspace=ws)
+        out32 = U.run_decode(st, t, out_dtype=torch.float32, workspace=ws)
+        U.assert_rounds(out, out32, f"{st.name} layer {layer}")
+        vals = {"q": qh, "k_cache": W.torch_to_host(dv["k_cache"], st.dtype),
+                "v_cache": W.torch_to_host(dv["v_cache"], st.dtype)}
+        del dv
+        worst = 0.0
+        for s in range(st.num_seqs):
+            want = U.oracle_decode(st, vals, seqs=[s])
+            g = U.to_f64(out32[s])
+            err = float(np.abs(g - want[s]).max()) if st.context_lens[s] > 0 else float(
+                np.abs(g).max())
+            worst = max(worst, err)
+            assert err <= U.TOL[st.dtype], f"{st.name} layer {layer} seq {s}: {err:.3e}"
+        U.say(f"  {st.name} layer {layer}: all {st.num_seqs} sequences, max|err| = {worst:.3e}")
 
 
 def test_full_llama3_8b_decode():
-    _full_size(W.llama3_8b_decode(0), 8, 1)
+    _full_size(W.llama3_8b_decode(0))
 
 
-def test_full_llama3_70b_decode_one_layer():
-    _full_size(W.llama3_70b_decode(0, layers=1), 3, 2)
+def test_full_llama3_70b_decode_layers_0_40_79():
+    _full_size(W.llama3_70b_decode(0), layers=(0, 40, 79))
 
 
 def test_full_shared_prefix_mix():
-    _full_size(W.shared_prefix_mix(0), 8, 3)
+    _full_size(W.shared_prefix_mix(0))
 
 
 def test_prepared_call_matches_decode():
