@@ -63,7 +63,8 @@ typedef enum {
   PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required       */
   PA_ERR_HIP = -5,         /* a HIP launch or runtime call failed              */
   PA_ERR_NO_BLOCKS = -6,   /* the block pool has too few free blocks           */
-  PA_ERR_INVALID = -7      /* unknown or released sequence id, bad block id    */
+  PA_ERR_INVALID = -7,     /* unknown or released sequence id, bad block id    */
+  PA_ERR_SCRATCH = -8      /* more scratch than paged_attn_decode_noalloc has  */
 } pa_status;
 
 /* PA_FP8_E4M3: 8-bit floating-point codes (sign, 4 exponent bits with bias 7,
@@ -111,6 +112,27 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
                       int max_context_len, float scale, int dtype, int out_dtype,
                       int partition_tokens, void* workspace, size_t workspace_bytes,
                       pa_stream_t stream);
+
+/*
+ * paged_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result and kernels as
+ * paged_attn_decode; the work plan and partials go to a scratch array of
+ * 32 MiB that the library holds in device memory, one per GPU, until the
+ * process ends.  The call allocates nothing.  A call that would need more
+ * scratch than that (the need depends on the batch, the heads and the device's
+ * resident waves; the Llama-3-8B/70B decode layers use under 14 MiB) returns
+ * PA_ERR_SCRATCH and enqueues nothing.  Every call on a GPU uses that GPU's one
+ * array and nothing in it needs to start at any value, but calls whose work may
+ * overlap on one GPU (several streams, several host threads) race on it and
+ * must be serialized by the caller.
+ */
+int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                              int block_size, int num_blocks, int max_blocks_per_seq,
+                              int max_context_len, float scale, int dtype, int out_dtype,
+                              int partition_tokens, pa_stream_t stream);
 
 /*
  * Several query tokens per sequence: the k guessed tokens that speculative

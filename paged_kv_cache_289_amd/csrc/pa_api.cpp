@@ -182,6 +182,9 @@ const char* paged_attn_status_string(int status) {
     case PA_ERR_HIP: return "HIP launch or runtime error";
     case PA_ERR_NO_BLOCKS: return "block pool has too few free blocks";
     case PA_ERR_INVALID: return "unknown or released sequence id, or block id outside the pool";
+    case PA_ERR_SCRATCH:
+      return "the call needs more device scratch than the allocation-free entry point holds "
+             "(32 MiB per GPU)";
     default: return "unknown status";
   }
 }
@@ -242,7 +245,11 @@ int decode_core(void* out, const void* q, const void* k_cache, const void* v_cac
                 int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                 int max_blocks_per_seq, int max_context_len, float scale, int dtype, int out_dtype,
                 int partition_tokens, void* workspace, size_t workspace_bytes, pa_stream_t stream,
-                float* lse, const pa::KernelEvents& ev, float out_scale = 1.f) {
+                float* lse, const pa::KernelEvents& ev, float out_scale = 1.f,
+                bool device_sized = false) {
+  // device_sized: the workspace is the allocation-free entry point's scratch,
+  // checked against what this device's launch needs (PA_ERR_SCRATCH if it is
+  // too small) rather than against the device-independent size.
   // (8-bit caches come with bf16 queries: the query type is what the checks see)
   int rc = check_attn_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                              max_blocks_per_seq, max_context_len,
@@ -278,17 +285,23 @@ int decode_core(void* out, const void* q, const void* k_cache, const void* v_cac
   if (num_seqs <= pa::kMaxSplitSeqs) {
     // the workspace is checked against the device-independent bound (what
     // paged_attn_workspace_size returns) before any HIP call
-    const int bound_waves = split_waves_bound(num_seqs, num_kv_heads, block_size,
-                                              max_context_len, partition_tokens);
-    const size_t need = split_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
-                                              bound_waves);
-    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
+    if (!device_sized) {
+      const int bound_waves = split_waves_bound(num_seqs, num_kv_heads, block_size,
+                                                max_context_len, partition_tokens);
+      const size_t need = split_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                bound_waves);
+      if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_ERR_WORKSPACE;
+    }
     // balanced split over the resident waves of this device
     const int wgs = pa::split_workgroups_per_cu(dtype, head_dim, block_size, a.group);
     const int resident = std::min(pa::kMaxSplitWaves,
                                   device_cus() * wgs * pa::kWaves);
     const SplitPlan sp = plan_split(num_seqs, num_kv_heads, block_size, max_context_len,
                                     partition_tokens, resident);
+    if (device_sized &&
+        workspace_bytes < split_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                sp.waves))
+      return PA_ERR_SCRATCH;
     split_workspace_ptrs(workspace, num_seqs, num_heads, num_kv_heads, head_dim, sp.waves, &a);
     a.chunk_blocks = sp.chunk;
     a.split_workgroups = sp.workgroups;
@@ -300,7 +313,7 @@ int decode_core(void* out, const void* q, const void* k_cache, const void* v_cac
     const int max_parts = std::max(1, ceil_div(max_context_len, part));
     const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, max_parts);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-      return PA_ERR_WORKSPACE;
+      return device_sized ? PA_ERR_SCRATCH : PA_ERR_WORKSPACE;
     if (need > 0) split_workspace(workspace, num_seqs, num_heads, max_parts, &a);
     a.part = part;
     a.max_parts = max_parts;
@@ -328,6 +341,29 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                      max_context_len, scale, dtype, out_dtype, partition_tokens, workspace,
                      workspace_bytes, stream, nullptr, t_events);
+}
+
+int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                              int block_size, int num_blocks, int max_blocks_per_seq,
+                              int max_context_len, float scale, int dtype, int out_dtype,
+                              int partition_tokens, pa_stream_t stream) {
+  // every scalar and pointer check before the first HIP call
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  const int rc = check_attn_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                   num_blocks, max_blocks_per_seq, max_context_len, dtype,
+                                   out_dtype, partition_tokens, scale);
+  if (rc != PA_OK) return rc;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
+  void* scratch = nullptr;
+  if (pa::scratch_buffer(&scratch) != hipSuccess) return PA_ERR_HIP;
+  return decode_core(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                     max_context_len, scale, dtype, out_dtype, partition_tokens, scratch,
+                     pa::kScratchBytes, stream, nullptr, t_events, 1.f, /*device_sized=*/true);
 }
 
 }  // extern "C"

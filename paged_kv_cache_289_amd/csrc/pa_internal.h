@@ -114,6 +114,13 @@ hipError_t launch_cascade_combine(void* out, const float* ws_ml, const float* ws
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int workgroups,
                               int nontemporal, hipStream_t stream);
 
+// Device scratch of the allocation-free decode entry point: kScratchBytes in
+// a file-scope device array, one copy per GPU (pa_noalloc.hip).  Returns the
+// current device's copy, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_buffer(void** ptr);
+
 hipError_t launch_check(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                         int block_size, int num_blocks, int max_blocks_per_seq,
                         int max_context_len, int32_t* bad_count, hipStream_t stream);

@@ -22,7 +22,7 @@ _LIB_PATH = os.environ.get("PAGED_ATTN_LIB") or \
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = \
     0, -1, -2, -3, -4, -5
-PA_ERR_NO_BLOCKS, PA_ERR_INVALID = -6, -7
+PA_ERR_NO_BLOCKS, PA_ERR_INVALID, PA_ERR_SCRATCH = -6, -7, -8
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 
 _TORCH_DT = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
@@ -33,6 +33,8 @@ SIGNATURES = {
     "paged_attn_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "paged_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                                _I, _I, _P, _Z, _P]),
+    "paged_attn_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                       _F, _I, _I, _I, _P]),
     "paged_attn_multiq": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                _I, _F, _I, _I, _I, _I, _P, _Z, _P]),
     "paged_kv_gather": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
@@ -198,6 +200,26 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                _dtype(q), _dtype(out), int(partition_tokens), _ptr(workspace),
                                wbytes, _stream(stream))
     _check("paged_attn_decode", rc)
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                   max_context_len: int, out: torch.Tensor, partition_tokens: int = 0,
+                   stream=None) -> torch.Tensor:
+    """:func:`decode` through ``paged_attn_decode_noalloc``: no workspace, the library's
+    per-GPU scratch instead; ``out`` must be given (nothing is allocated)."""
+    _need_contig(q=q, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                 context_lens=context_lens, out=out)
+    S, H, D = q.shape
+    NB, Hk, B, _ = k_cache.shape
+    _same_dtype(q, k_cache, v_cache)
+    rc = LIB.paged_attn_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(block_tables), _ptr(context_lens), S, H, Hk, D, B,
+                                       NB, block_tables.shape[1], int(max_context_len),
+                                       float(scale), _dtype(q), _dtype(out),
+                                       int(partition_tokens), _stream(stream))
+    _check("paged_attn_decode_noalloc", rc)
     return out
 
 

@@ -41,6 +41,7 @@ hipError_t launch_cascade_combine(void*, const float*, const float*, int, int, c
 hipError_t launch_stream_read(const void*, size_t, unsigned*, int, int, hipStream_t) {
   return hipErrorNoDevice;
 }
+hipError_t scratch_buffer(void**) { return hipErrorNoDevice; }
 hipError_t launch_check(const int32_t*, const int32_t*, int, int, int, int, int, int32_t*,
                         hipStream_t) {
   return hipErrorNoDevice;

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4, -5, -6, -7):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert ops.status_string(st)
     assert ops.status_string(-99) == "unknown status"
 
@@ -94,6 +94,26 @@ def test_binding_rejects_cache_dtype_other_than_the_query():
     with pytest.raises(ops.PagedAttnError):
         ops.multiq(q, codes.view(torch.float16), codes.view(torch.float16), tbl, lens, qoff, 0.1,
                    16, 1)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), ops.PA_ERR_NULL),
+    (dict(S=-1), ops.PA_ERR_SHAPE),
+    (dict(D=96), ops.PA_ERR_UNSUPPORTED),
+    (dict(dt=3), ops.PA_ERR_UNSUPPORTED),
+    (dict(H=30, Hk=8), ops.PA_ERR_SHAPE),
+    (dict(q=ctypes.c_void_p(0x10008)), ops.PA_ERR_UNSUPPORTED),
+    (dict(S=0, q=None, out=None), ops.PA_OK),
+])
+def test_noalloc_decode_rejects_bad_arguments_on_host(kw, code):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tbl=FAKE, lens=FAKE, S=4, H=32, Hk=8, D=128, B=16,
+             NB=100, mbs=64, maxctx=1024, scale=0.088, dt=ops.PA_BF16, odt=ops.PA_BF16, part=0,
+             stream=None)
+    a.update(kw)
+    assert ops.LIB.paged_attn_decode_noalloc(
+        a["out"], a["q"], a["k"], a["v"], a["tbl"], a["lens"], a["S"], a["H"], a["Hk"], a["D"],
+        a["B"], a["NB"], a["mbs"], a["maxctx"], a["scale"], a["dt"], a["odt"], a["part"],
+        a["stream"]) == code
 
 
 def test_decode_with_no_sequences_is_a_no_op():
