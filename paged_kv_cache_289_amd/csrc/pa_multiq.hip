@@ -229,10 +229,33 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
   // between global memory and LDS would pass through private memory.
   const int spid = ROWS ? tid : lane;  // this thread's staging index
   const int scol = spid % CPR;         // its 16-byte column
+  // Chunk i of this thread: token tok_i of the tile, i.e. block tok_i / B of
+  // the tile at slot tok_i % B; its byte offset inside a block of the pool
+  // (head g, that slot, this column) is the same for every full tile.
+  const size_t blk_stride = (size_t)Hk * B * kRowBytes;   // one physical block, all heads
+  int chunk_off[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int tok = spid / CPR + i * (NP / CPR);
+    chunk_off[i] = (g * B + tok % B) * kRowBytes + scol * 16;
+  }
   auto stage_load = [&](int t0, u32x4_t (&sk)[kPer], u32x4_t (&sv)[kPer]) {
     int ids[kTileBlocks];
 #pragma unroll
     for (int k = 0; k < kTileBlocks; ++k) ids[k] = tblc[min(t0 / B + k, jlast)];
+    if (t0 + 32 <= L) {   // workgroup-uniform: a full tile (block ids from scalar loads)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int jt = (spid / CPR + i * (NP / CPR)) / B;
+        int phys = ids[0];
+#pragma unroll
+        for (int k = 1; k < kTileBlocks; ++k) phys = (jt == k) ? ids[k] : phys;
+        const size_t boff = (size_t)phys * blk_stride;
+        sk[i] = *reinterpret_cast<const u32x4_t*>(kbase + boff + chunk_off[i]);
+        sv[i] = *reinterpret_cast<const u32x4_t*>(vbase + boff + chunk_off[i]);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int tok = spid / CPR + i * (NP / CPR);
@@ -246,7 +269,9 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
       sv[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
     }
   };
-  constexpr int kLdsBytes = ROWS ? 2 * kStageBytes : 16;   // (only the rows layout stages)
+  // rows layout: 32-token tiles per loop step, and two LDS stages of a step each
+  constexpr int kTps = 1;
+  constexpr int kLdsBytes = ROWS ? 2 * kTps * kStageBytes : 16;   // (only the rows layout stages)
   __shared__ __attribute__((aligned(16))) char sm_kv[kLdsBytes];
   // base: K tile, base + kTileBytes: V tile
   auto stage_store = [&](char* base, const u32x4_t (&sk)[kPer], const u32x4_t (&sv)[kPer]) {
@@ -286,15 +311,17 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
       }
   };
 
-  // QK^T, masking and the online softmax of one tile; returns the P^T operands
-  // (pb: p rounded or cut to the input dtype, pl: bf16 residual)
-  auto softmax_tile = [&](int t0, const uint4 (&kr)[KS], uint4& pb0, uint4& pb1, uint4& pl0,
-                          uint4& pl1) {
-    // S^T = K Q^T: lane holds tokens t0 + tile_token(v, hh) of its row
+  // S^T = K Q^T of one tile: lane holds tokens t0 + tile_token(v, hh) of its row
+  auto qk_tile = [&](const uint4 (&kr)[KS]) {
     f32x16_t sc = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) sc = M::mma(kr[ks], qv[ks], sc);
-
+    return sc;
+  };
+  // masking and the online softmax of one tile's scores; returns the P^T
+  // operands (pb: p rounded or cut to the input dtype, pl: bf16 residual)
+  auto softmax_scores = [&](int t0, f32x16_t sc, uint4& pb0, uint4& pb1, uint4& pl0,
+                            uint4& pl1) {
     float mx = kNegInf;
     if (t0 + 32 <= min(l_tile_min, tok_end)) {   // wave-uniform: no key of the tile is masked
 #pragma unroll
@@ -358,7 +385,7 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
   // token layout: V rows in registers (token mcol) -> V^T through the identity
   auto compute_tile = [&](int t0, const uint4 (&kr)[KS], const uint4 (&vr)[KS]) {
     uint4 pb0, pb1, pl0, pl1;
-    softmax_tile(t0, kr, pb0, pb1, pl0, pl1);
+    softmax_scores(t0, qk_tile(kr), pb0, pb1, pl0, pl1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       // V I reproduces the V values exactly, so repacking them is exact
@@ -369,39 +396,56 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
   };
 
   if constexpr (ROWS) {
-    // All four waves walk the workgroup's tiles [tok0, wg_end) in step: tile
-    // i is read from LDS buffer i % 2 while tile i + 1 is loaded into
-    // registers and then stored to the other buffer; one barrier per tile.
-    // The loop bounds are workgroup-uniform, so every wave reaches every
-    // barrier, and the last tile is peeled off so that every load in the loop
-    // is unconditional.
+    // All four waves walk the workgroup's tokens [tok0, wg_end) in step, kTps
+    // 32-token tiles per step: the step's tiles are read from one LDS stage
+    // while the next step's are loaded into registers and then stored to the
+    // other stage; one barrier per step.  The loop bounds are
+    // workgroup-uniform, so every wave reaches every barrier, and the last
+    // step is peeled off so that every load in the loop is unconditional.
+    // (A wave whose rows see no key of a tile skips its compute; a tile of a
+    // step that starts past the last key loads the step's first tile again
+    // and is skipped.)
     auto compute_from = [&](int t0, const char* base) {
       if (t0 < tok_end) {   // wave-uniform: the wave's rows see keys in this tile
         uint4 kr[KS], va[DB][2];
         lds_read_k(base, kr);
         lds_read_vt(base, va);
         uint4 pb0, pb1, pl0, pl1;
-        softmax_tile(t0, kr, pb0, pb1, pl0, pl1);
+        softmax_scores(t0, qk_tile(kr), pb0, pb1, pl0, pl1);
 #pragma unroll
         for (int db = 0; db < DB; ++db) pv_block(db, va[db][0], va[db][1], pb0, pb1, pl0, pl1);
       }
     };
+    auto load_step = [&](int t0, u32x4_t (&sk)[kTps][kPer], u32x4_t (&sv)[kTps][kPer]) {
+#pragma unroll
+      for (int u = 0; u < kTps; ++u) stage_load(t0 + 32 * u < L ? t0 + 32 * u : t0, sk[u], sv[u]);
+    };
+    auto store_step = [&](char* base, const u32x4_t (&sk)[kTps][kPer],
+                          const u32x4_t (&sv)[kTps][kPer]) {
+#pragma unroll
+      for (int u = 0; u < kTps; ++u) stage_store(base + u * kStageBytes, sk[u], sv[u]);
+    };
+    auto compute_step = [&](int t0, const char* base) {
+#pragma unroll
+      for (int u = 0; u < kTps; ++u) compute_from(t0 + 32 * u, base + u * kStageBytes);
+    };
+    constexpr int kStep = 32 * kTps;
     int t0 = tok0;
     int buf = 0;
-    u32x4_t sk[kPer], sv[kPer];
-    stage_load(t0, sk, sv);
-    stage_store(sm_kv, sk, sv);
+    u32x4_t sk[kTps][kPer], sv[kTps][kPer];
+    load_step(t0, sk, sv);
+    store_step(sm_kv, sk, sv);
     __syncthreads();
-    while (t0 + 32 < wg_end) {
-      stage_load(t0 + 32, sk, sv);
+    while (t0 + kStep < wg_end) {
+      load_step(t0 + kStep, sk, sv);
       __builtin_amdgcn_sched_barrier(0);
-      compute_from(t0, sm_kv + buf * kStageBytes);
+      compute_step(t0, sm_kv + buf * kTps * kStageBytes);
       buf ^= 1;
-      stage_store(sm_kv + buf * kStageBytes, sk, sv);
+      store_step(sm_kv + buf * kTps * kStageBytes, sk, sv);
       __syncthreads();
-      t0 += 32;
+      t0 += kStep;
     }
-    compute_from(t0, sm_kv + buf * kStageBytes);
+    compute_step(t0, sm_kv + buf * kTps * kStageBytes);
   } else {
     // Each wave takes tiles tok0 + 32 wave, + 32 kWaves, ... and loads them
     // straight into registers in the operand layout (lane (mcol, hh) reads
