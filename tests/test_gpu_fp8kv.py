@@ -51,8 +51,9 @@ def test_fp8kv_decode(D, B, G):
     for ks, vs in ((1.0, 1.0), (0.37, 2.5)):
         want = OP.paged_decode_quant_kv(vals["q"], "bf16", k8, v8, "fp8e4m3", ks, vs,
                                         st.block_tables, st.context_lens, B, st.scale)
-        U.assert_close(_run(st, t, ks, vs, torch.float32), want, "bf16", f"scales {ks},{vs}")
-        U.assert_close(_run(st, t, ks, vs), want, "bf16", f"scales {ks},{vs} bf16 out")
+        out32 = _run(st, t, ks, vs, torch.float32)
+        U.assert_close(out32, want, "bf16", f"scales {ks},{vs}")
+        U.assert_rounds(_run(st, t, ks, vs), out32, f"scales {ks},{vs} bf16 out")
 
 
 def test_fp8kv_forced_pieces_and_edges():
@@ -98,12 +99,15 @@ def test_full_llama3_8b_decode_fp8kv():
          "block_tables": torch.from_numpy(st.block_tables).to(U.DEV),
          "context_lens": torch.from_numpy(st.context_lens).to(U.DEV)}
     out = _run(st, t, 0.5, 2.0, torch.float32)
+    U.assert_rounds(_run(st, t, 0.5, 2.0), out, "llama3 8b fp8 bf16 out")
     q = W.torch_to_host(dv["q"], "bf16")
     k8, v8 = t["k8"].cpu().numpy(), t["v8"].cpu().numpy()
-    pick = sorted({int(np.argmax(st.context_lens)), int(np.argmin(st.context_lens)), 5, 40})
-    want = OP.paged_decode_quant_kv(q, "bf16", k8, v8, "fp8e4m3", 0.5, 2.0, st.block_tables,
-                                    st.context_lens, st.block_size, st.scale, seqs=pick)
-    U.assert_close(out, want, "bf16", "llama3 8b fp8", rows=pick)
+    del dv, t
+    U.assert_all_seqs(
+        out, lambda s: OP.paged_decode_quant_kv(q, "bf16", k8, v8, "fp8e4m3", 0.5, 2.0,
+                                                st.block_tables, st.context_lens,
+                                                st.block_size, st.scale, seqs=[s]),
+        st, "llama3 8b fp8", U.TOL["bf16"])
 
 
 def test_fp8_caches_through_the_byte_movers():

@@ -37,7 +37,7 @@ def test_shared_prefix_decode(dtype, D, B, G):
     want = U.oracle_decode(st, vals)
     out = _run(st, t, P, torch.float32)
     U.assert_close(out, want, dtype, "cascade f32 out")
-    U.assert_close(_run(st, t, P), want, dtype, f"cascade {dtype} out")
+    U.assert_rounds(_run(st, t, P), out, f"cascade {dtype} out")
     dec = U.run_decode(st, t, out_dtype=torch.float32)
     assert np.max(np.abs(U.to_f64(out) - U.to_f64(dec))) <= 2 * U.TOL[dtype]
 
@@ -65,8 +65,9 @@ def test_shared_prefix_long_prefix_many_rows():
     t = U.upload(st, vals)
     seqs = [0, 7, 39]
     want = U.oracle_decode(st, vals, seqs=seqs)
-    U.assert_close(_run(st, t, 300, torch.float32), want, "bf16", "P=300", rows=seqs)
-    U.assert_close(_run(st, t, 300), want, "bf16", "P=300 bf16 out", rows=seqs)
+    out32 = _run(st, t, 300, torch.float32)
+    U.assert_close(out32, want, "bf16", "P=300", rows=seqs)
+    U.assert_rounds(_run(st, t, 300), out32, "P=300 bf16 out")
 
 
 def test_full_shared_prefix_mix_cascade():
@@ -78,8 +79,8 @@ def test_full_shared_prefix_mix_cascade():
     t["context_lens"] = torch.from_numpy(st.context_lens).to(U.DEV)
     out = _run(st, t, 128)
     out32 = _run(st, t, 128, torch.float32)
+    U.assert_rounds(out, out32, "shared prefix mix bf16 out")
     vals = {k: W.torch_to_host(v, st.dtype) for k, v in dv.items()}
-    pick = sorted({int(np.argmax(st.context_lens)), int(np.argmin(st.context_lens)), 0, 101, 255})
-    want = U.oracle_decode(st, vals, seqs=pick)
-    U.assert_close(out32, want, st.dtype, "shared prefix mix f32 out", rows=pick)
-    U.assert_close(out, want, st.dtype, "shared prefix mix bf16 out", rows=pick)
+    del dv, t
+    U.assert_all_seqs(out32, lambda s: U.oracle_decode(st, vals, seqs=[s]), st,
+                      "shared prefix mix f32 out", U.TOL[st.dtype])
