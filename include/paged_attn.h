@@ -254,8 +254,8 @@ int paged_attn_decode_shared_prefix(void* out, const void* q, const void* k_cach
  * q is bf16 [num_seqs][num_heads][head_dim] (converted to f16 in the kernel:
  * exact for |q| in f16's normal range); out_dtype is PA_F32 or PA_BF16.
  * Accumulation is fp32.  Codes are widened exactly; the NaN codes are not
- * supported.  Supported: head_dim 128 with block_size 8/16/32, head_dim 64
- * with block_size 16/32, groups num_heads / num_kv_heads of at most 8.
+ * supported.  Supported: head_dim 64 and 128 with block_size 8/16/32,
+ * groups num_heads / num_kv_heads of at most 8.
  * partition_tokens, the workspace (paged_attn_workspace_size(...) for the same
  * shapes and partition_tokens) and the errors are as for paged_attn_decode,
  * plus PA_ERR_SHAPE for k_scale or v_scale not finite and positive.

@@ -594,7 +594,6 @@ int paged_attn_decode_fp8kv(void* out, const void* q, const void* k_cache, const
       !(v_scale > 0.f))
     return PA_ERR_SHAPE;
   if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
-  if (head_dim == 64 && block_size == 8) return PA_ERR_UNSUPPORTED;
   if (num_kv_heads > 0 && num_heads % num_kv_heads == 0 && num_heads / num_kv_heads > 8)
     return PA_ERR_UNSUPPORTED;
   // the tensor scales go into the score scale and the output factor

@@ -44,6 +44,7 @@ constexpr float kMaxInit = -1e30f;
 template <int DT> struct Elem;
 
 template <> struct Elem<PA_F32> {
+  typedef uint4 Vec;    // a lane's share of one token row: one 16-byte vector
   typedef uint4 QVec;   // the query in the same type, one 16-byte vector
   __device__ static inline QVec load_q(const void* q, size_t idx) {
     return reinterpret_cast<const uint4*>(q)[idx / kPerVec];
@@ -79,6 +80,7 @@ __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 template <> struct Elem<PA_BF16> {
+  typedef uint4 Vec;    // a lane's share of one token row: one 16-byte vector
   typedef uint4 QVec;   // the query in the same type, one 16-byte vector
   __device__ static inline QVec load_q(const void* q, size_t idx) {
     return reinterpret_cast<const uint4*>(q)[idx / kPerVec];
@@ -117,6 +119,7 @@ template <> struct Elem<PA_BF16> {
 };
 
 template <> struct Elem<PA_F16> {
+  typedef uint4 Vec;    // a lane's share of one token row: one 16-byte vector
   typedef uint4 QVec;   // the query in the same type, one 16-byte vector
   __device__ static inline QVec load_q(const void* q, size_t idx) {
     return reinterpret_cast<const uint4*>(q)[idx / kPerVec];
@@ -156,18 +159,22 @@ template <> struct Elem<PA_F16> {
   }
 };
 
-// 8-bit E4M3 keys and values, with bf16 queries.  A 16-byte vector holds 16
-// codes.  gfx950 widens two codes per instruction: v_cvt_scalef32_pk_f16_fp8
-// to an f16 pair (every E4M3 value is exact in f16) for QK as v_dot2_f32_f16
-// against the query held as f16 pairs, and v_cvt_pk_f32_fp8 to two fp32
-// values for PV.  The NaN codes are not supported.
+// 8-bit E4M3 keys and values, with bf16 queries.  A lane holds 8 codes of a
+// token row (an 8-byte vector), so a row of 128 codes is 16 lanes, one DPP
+// row, as for the 16-bit types: the same reduce-scatter of the scores, and a
+// lane's accumulators and query cover 8 dims.  gfx950 widens two codes per
+// instruction: v_cvt_scalef32_pk_f16_fp8 to an f16 pair (every E4M3 value is
+// exact in f16) for QK as v_dot2_f32_f16 against the query held as f16 pairs,
+// and v_cvt_pk_f32_fp8 to two fp32 values for PV.  The NaN codes are not
+// supported.
 struct Fp8Q {
-  uint32_t w[8];   // 16 query values as f16 pairs
+  uint32_t w[4];   // 8 query values as f16 pairs
 };
 
 template <> struct Elem<PA_FP8_E4M3> {
   static constexpr int kBytes = 1;
-  static constexpr int kPerVec = 16;
+  static constexpr int kPerVec = 8;
+  typedef uint2 Vec;
   typedef Fp8Q QVec;
   __device__ static inline float dot2(uint32_t a, uint32_t b, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
@@ -178,20 +185,20 @@ template <> struct Elem<PA_FP8_E4M3> {
   __device__ static inline uint32_t f16_pair(uint32_t x) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HI));
   }
-  __device__ static inline float dot0(const QVec& q, const uint4& k) {
-    const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = dot2(q.w[2 * i], f16_pair<false>(kw[i]), acc);
-      acc = dot2(q.w[2 * i + 1], f16_pair<true>(kw[i]), acc);
-    }
+  // (first step in the three-operand form with an inline zero, as for f16)
+  __device__ static inline float dot0(const QVec& q, const uint2& k) {
+    float acc;
+    const uint32_t k0 = f16_pair<false>(k.x);
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(acc) : "v"(q.w[0]), "v"(k0));
+    acc = dot2(q.w[1], f16_pair<true>(k.x), acc);
+    acc = dot2(q.w[2], f16_pair<false>(k.y), acc);
+    acc = dot2(q.w[3], f16_pair<true>(k.y), acc);
     return acc;
   }
-  __device__ static inline void to_float(const uint4& v, float* f) {
-    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+  __device__ static inline void to_float(const uint2& v, float* f) {
+    const uint32_t vw[2] = {v.x, v.y};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(vw[i], false);
       const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(vw[i], true);
       f[4 * i] = lo[0];
@@ -200,15 +207,14 @@ template <> struct Elem<PA_FP8_E4M3> {
       f[4 * i + 3] = hi[1];
     }
   }
-  // 16 bf16 query values starting at element `idx` (16-element aligned), as f16
+  // 8 bf16 query values starting at element `idx` (8-element aligned), as f16
   // pairs (rounded to nearest; bf16 values within f16's range convert exactly)
   __device__ static inline QVec load_q(const void* q, size_t idx) {
-    const uint4* p = reinterpret_cast<const uint4*>(q) + idx / 8;
-    const uint4 a = p[0], b = p[1];
-    const uint32_t src[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint4 a = reinterpret_cast<const uint4*>(q)[idx / 8];
+    const uint32_t src[4] = {a.x, a.y, a.z, a.w};
     QVec r;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       typedef float f2_t __attribute__((ext_vector_type(2)));
       const f2_t f = {bf16_lo(src[i]), bf16_hi(src[i])};
       r.w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
@@ -218,12 +224,12 @@ template <> struct Elem<PA_FP8_E4M3> {
   __device__ static inline QVec zero_q() {
     QVec r;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.w[i] = 0u;
+    for (int i = 0; i < 4; ++i) r.w[i] = 0u;
     return r;
   }
   __device__ static inline void flip_q(QVec& q) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q.w[i] ^= 0x80008000u;
+    for (int i = 0; i < 4; ++i) q.w[i] ^= 0x80008000u;
   }
 };
 
@@ -385,6 +391,7 @@ __device__ inline ConstI32Ptr as_const(const int32_t* p) { return (ConstI32Ptr)p
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 // Descriptor word 3 for untyped dword access on gfx9-family parts.
 constexpr int kBufferWord3 = 0x00020000;
@@ -398,16 +405,24 @@ __device__ inline BufRsrc make_rsrc(const void* base, int nbytes) {
                                            kBufferWord3);
 }
 
-__device__ inline uint4 buffer_load16(BufRsrc r, int byte_off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+// One lane vector (16 or 8 bytes) through a buffer descriptor, with or without
+// the non-temporal hint.
+template <typename V, bool NT> __device__ inline V buffer_load_vec(BufRsrc r, int off, int coff);
+template <> __device__ inline uint4 buffer_load_vec<uint4, false>(BufRsrc r, int off, int coff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, coff, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-
-// The same load with the non-temporal hint (nt): the line is read once, so the
-// caches should not keep it at the expense of data that is reused.
-__device__ inline uint4 buffer_load16_nt(BufRsrc r, int byte_off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCpolNt);
+template <> __device__ inline uint4 buffer_load_vec<uint4, true>(BufRsrc r, int off, int coff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, coff, kCpolNt);
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <> __device__ inline uint2 buffer_load_vec<uint2, false>(BufRsrc r, int off, int coff) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, coff, 0);
+  return make_uint2(v.x, v.y);
+}
+template <> __device__ inline uint2 buffer_load_vec<uint2, true>(BufRsrc r, int off, int coff) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, coff, kCpolNt);
+  return make_uint2(v.x, v.y);
 }
 
 }  // namespace pa

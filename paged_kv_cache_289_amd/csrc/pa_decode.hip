@@ -60,6 +60,7 @@ __device__ inline float exp_scale(float scale_log2) {
 template <int DT, int D, int B, int GP>
 struct DecodeWave {
   using E = Elem<DT>;
+  using Vec = typename E::Vec;             // a lane's vector of one token row
   static constexpr int EPL = E::kPerVec;   // elements per lane per token
   static constexpr int LPT = D / EPL;      // lanes per token row
   static constexpr int TPL = 64 / LPT;     // token rows per wave
@@ -159,7 +160,7 @@ struct DecodeWave {
   // two always hold the same set of values, and halving by bits 3, 2, 1, 0 in
   // turn leaves lane c with entries kM c .. kM c + kM - 1 of the initial order,
   // which therefore holds score c + 16 k at entry kM c + k.
-  __device__ void scores_scatter(const uint4 (&kr)[LPB], float (&own)[kScoresPerLane]) const {
+  __device__ void scores_scatter(const Vec (&kr)[LPB], float (&own)[kScoresPerLane]) const {
     constexpr int kM = kScoresPerLane;
     float x[kScores];
 #pragma unroll
@@ -178,7 +179,7 @@ struct DecodeWave {
   // One block with reduce-scattered scores: QK, the online softmax on the
   // lane's own scores (head col % GP) and PV with the row's weights broadcast
   // back from the lanes that evaluated them.
-  __device__ void compute_block_scatter(int jj, const uint4 (&kr)[LPB], const uint4 (&vr)[LPB],
+  __device__ void compute_block_scatter(int jj, const Vec (&kr)[LPB], const Vec (&vr)[LPB],
                                         int L, float c) {
     constexpr int kM = kScoresPerLane;
     float own[kM];
@@ -265,37 +266,32 @@ struct DecodeWave {
     uint64_t colbit[4];   // lanes whose column has bit b set (for own_score)
 #pragma unroll
     for (int b = 0; b < 4; ++b) colbit[b] = __builtin_amdgcn_ballot_w64((col >> b) & 1);
-    uint4 kbuf[NBUF][LPB], vbuf[NBUF][LPB];
+    Vec kbuf[NBUF][LPB], vbuf[NBUF][LPB];
     // The lane's byte offset inside a (block, KV head) slice for its first
-    // load; load i adds a constant, which the loads carry as their immediate
-    // offset (one offset register for all of them).
-    const int voff0 = row * kRowBytes + col * 16;
-    auto load_block = [&](int jj, int phys, bool in_range, uint4 (&kr)[LPB], uint4 (&vr)[LPB]) {
+    // load; load i adds a constant, which goes in the load's scalar/immediate
+    // offset, so all loads share one offset register that nothing in the ring
+    // ever writes.  (A register written at the top of the ring would have to
+    // wait for every load still pending into it on any path, which the
+    // compiler covers by draining the whole ring there.)
+    const int voff0 = row * kRowBytes + col * (int)sizeof(Vec);
+    auto load_block = [&](int jj, int phys, bool in_range, Vec (&kr)[LPB], Vec (&vr)[LPB]) {
       // the slots below L (wave-uniform; at least one for a block in range)
       const int nrec = in_range ? min(L - jj * B, B) * kRowBytes : 0;
       const size_t boff = (size_t)phys * blk_bytes;
       const BufRsrc rk = make_rsrc(kbase + boff, nrec);
       const BufRsrc rv = make_rsrc(vbase + boff, nrec);
-      // (opaque here, so that the per-load constants below stay next to the
-      // loads and fold into their immediate offsets instead of each being
-      // hoisted into a register of its own)
-      int vo = voff0;
-      asm volatile("" : "+v"(vo));
-      int voff[LPB];
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) voff[i] = vo + i * TPL * kRowBytes;
       // keep the issue order K then V, and both ahead of the compute that
       // follows, so each wait covers exactly the buffer being consumed
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) kr[i] = NT ? buffer_load16_nt(rk, voff[i]) : buffer_load16(rk, voff[i]);
+      for (int i = 0; i < LPB; ++i) kr[i] = buffer_load_vec<Vec, NT>(rk, voff0, i * TPL * kRowBytes);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) vr[i] = NT ? buffer_load16_nt(rv, voff[i]) : buffer_load16(rv, voff[i]);
+      for (int i = 0; i < LPB; ++i) vr[i] = buffer_load_vec<Vec, NT>(rv, voff0, i * TPL * kRowBytes);
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    auto compute_block = [&](int jj, const uint4 (&kr)[LPB], const uint4 (&vr)[LPB]) {
+    auto compute_block = [&](int jj, const Vec (&kr)[LPB], const Vec (&vr)[LPB]) {
       if constexpr (kScatter) {
         compute_block_scatter(jj, kr, vr, L, c);
         return;
@@ -882,16 +878,12 @@ static auto with_config(int dtype, int head_dim, int block_size, int group, F&& 
     if (group <= 2) return f(dt, d, b, std::integral_constant<int, 2>{});
     if (group <= 4) return f(dt, d, b, std::integral_constant<int, 4>{});
     if (group <= 8) return f(dt, d, b, std::integral_constant<int, 8>{});
-    // (8-bit caches stop at groups of 8: a lane's 16-element rows for 16 heads
-    // would not fit the register file; the host rejects them)
+    // (8-bit caches stop at groups of 8; the host rejects larger groups)
     constexpr bool kNo16 = decltype(dt)::value == PA_FP8_E4M3;
     return f(dt, d, b, std::integral_constant<int, kNo16 ? 8 : 16>{});
   };
   auto by_b = [&](auto dt, auto d) {
-    // (8-bit codes at head_dim 64 fill 16 tokens per wave load, more than an
-    // 8-token block: the host rejects that pair, the 16-token instance stands in)
-    constexpr bool kNo8 = decltype(dt)::value == PA_FP8_E4M3 && decltype(d)::value == 64;
-    if (block_size == 8 && !kNo8) return by_g(dt, d, std::integral_constant<int, kNo8 ? 16 : 8>{});
+    if (block_size == 8) return by_g(dt, d, std::integral_constant<int, 8>{});
     if (block_size == 16) return by_g(dt, d, std::integral_constant<int, 16>{});
     return by_g(dt, d, std::integral_constant<int, 32>{});
   };

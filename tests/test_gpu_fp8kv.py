@@ -40,7 +40,7 @@ def _run(st, t, ks, vs, out_dtype=None, part=0):
     return out
 
 
-CASES = [(D, B) for D in (64, 128) for B in (8, 16, 32) if not (D == 64 and B == 8)]
+CASES = [(D, B) for D in (64, 128) for B in (8, 16, 32)]
 
 
 @pytest.mark.parametrize("D,B", CASES)
@@ -80,7 +80,7 @@ def test_fp8kv_rejects_unsupported():
     S, H, D = t["q"].shape
     base = [None, None, None, None, None, None, S, H, 2, D, 16, st.num_blocks, 8, 64, 0.1, 1.0,
             1.0, o.PA_F32, 0, None, 0, None]
-    for k, v, code in ((10, 8, o.PA_ERR_UNSUPPORTED), (15, 0.0, o.PA_ERR_SHAPE),
+    for k, v, code in ((9, 96, o.PA_ERR_UNSUPPORTED), (15, 0.0, o.PA_ERR_SHAPE),
                        (16, float("inf"), o.PA_ERR_SHAPE), (17, o.PA_F16, o.PA_ERR_UNSUPPORTED)):
         args = list(base)
         args[k] = v
