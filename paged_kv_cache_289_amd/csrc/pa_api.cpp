@@ -246,10 +246,15 @@ int decode_core(void* out, const void* q, const void* k_cache, const void* v_cac
                 int max_blocks_per_seq, int max_context_len, float scale, int dtype, int out_dtype,
                 int partition_tokens, void* workspace, size_t workspace_bytes, pa_stream_t stream,
                 float* lse, const pa::KernelEvents& ev, float out_scale = 1.f,
-                bool device_sized = false) {
+                bool device_sized = false, int len_offset = 0, bool split_no_merge = false,
+                pa::AttnArgs* used = nullptr) {
   // device_sized: the workspace is the allocation-free entry point's scratch,
   // checked against what this device's launch needs (PA_ERR_SCRATCH if it is
   // too small) rather than against the device-independent size.
+  // len_offset: subtracted from every context length (the tails of a
+  // shared-prefix decode).  split_no_merge: with the balanced split, leave the
+  // pieces in the workspace (the caller merges them); `used` receives the
+  // launch's arguments (plan and workspace regions).
   // (8-bit caches come with bf16 queries: the query type is what the checks see)
   int rc = check_attn_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                              max_blocks_per_seq, max_context_len,
@@ -281,6 +286,7 @@ int decode_core(void* out, const void* q, const void* k_cache, const void* v_cac
   a.out_dtype = out_dtype;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.lse = lse;
+  a.len_offset = len_offset;
 
   if (num_seqs <= pa::kMaxSplitSeqs) {
     // the workspace is checked against the device-independent bound (what
@@ -307,6 +313,7 @@ int decode_core(void* out, const void* q, const void* k_cache, const void* v_cac
     a.split_workgroups = sp.workgroups;
     a.part = 0;
     a.max_parts = 0;
+    a.no_merge = split_no_merge ? 1 : 0;
   } else {
     const int part = resolve_partition(partition_tokens, num_seqs, num_heads, num_kv_heads,
                                        block_size, max_context_len, 1);
@@ -319,6 +326,7 @@ int decode_core(void* out, const void* q, const void* k_cache, const void* v_cac
     a.max_parts = max_parts;
     a.plan = nullptr;
   }
+  if (used) *used = a;
   hipError_t e = pa::launch_decode(dtype, head_dim, block_size, a.group, num_seqs, a,
                                    static_cast<hipStream_t>(stream), ev);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -377,7 +385,11 @@ int multiq_core(void* out, const void* q, const void* k_cache, const void* v_cac
                 int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                 int max_blocks_per_seq, int max_context_len, float scale, int causal, int dtype,
                 int out_dtype, int partition_tokens, void* workspace, size_t workspace_bytes,
-                pa_stream_t stream, float* lse, const pa::KernelEvents& ev, int no_merge = 0) {
+                pa_stream_t stream, float* lse, const pa::KernelEvents& ev, int no_merge = 0,
+                int fixed_rows = 0) {
+  // fixed_rows > 0: one sequence of fixed_rows query rows whose length is
+  // max_context_len (context_lens and q_offsets unused); only with no_merge
+  if (fixed_rows > 0 && (!no_merge || num_seqs != 1 || total_q != fixed_rows)) return PA_ERR_SHAPE;
   int rc = check_attn_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                              max_blocks_per_seq, max_context_len, dtype, out_dtype,
                              partition_tokens, scale);
@@ -385,7 +397,8 @@ int multiq_core(void* out, const void* q, const void* k_cache, const void* v_cac
   if (total_q < 0 || max_q_len < 0 || (total_q > 0 && max_q_len < 1)) return PA_ERR_SHAPE;
   if ((int64_t)max_q_len * num_seqs < total_q) return PA_ERR_SHAPE;
   if (num_seqs == 0 || total_q == 0) return PA_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !q_offsets)
+  if (!out || !q || !k_cache || !v_cache || !block_tables ||
+      (fixed_rows == 0 && (!context_lens || !q_offsets)))
     return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
 
@@ -423,6 +436,7 @@ int multiq_core(void* out, const void* q, const void* k_cache, const void* v_cac
   a.out_scale = 1.f;
   a.lse = lse;
   a.no_merge = no_merge;
+  a.fixed_rows = fixed_rows;
   hipError_t e = pa::launch_multiq(dtype, head_dim, block_size, a.group, num_seqs, a,
                                    static_cast<hipStream_t>(stream), ev);
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
@@ -479,7 +493,7 @@ namespace {
 // workspaces of the prefix multi-query call and of the tail decode, each
 // starting on a 256-byte boundary.
 struct CascadeLayout {
-  size_t ints = 0, out1 = 0, out2 = 0, lse1 = 0, lse2 = 0, mq = 0, dec = 0, total = 0;
+  size_t out1 = 0, out2 = 0, lse1 = 0, lse2 = 0, mq = 0, dec = 0, total = 0;
   size_t mq_bytes = 0, dec_bytes = 0;
 };
 
@@ -489,7 +503,6 @@ CascadeLayout cascade_layout(int num_seqs, int num_heads, int num_kv_heads, int 
   const size_t S = (size_t)num_seqs, rows = S * num_heads;
   const int prefix_tokens = prefix_blocks * block_size;
   size_t off = 0;
-  c.ints = off;  off = align256(off + (3 + S) * sizeof(int32_t));
   c.out1 = off;  off = align256(off + rows * head_dim * sizeof(float));
   c.out2 = off;  off = align256(off + rows * head_dim * sizeof(float));
   c.lse1 = off;  off = align256(off + rows * sizeof(float));
@@ -550,36 +563,54 @@ int paged_attn_decode_shared_prefix(void* out, const void* q, const void* k_cach
                                          max_context_len, prefix_blocks);
   if (!workspace || workspace_bytes < c.total || !aligned16(workspace)) return PA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  int32_t* ints = reinterpret_cast<int32_t*>(ws + c.ints);
   float* o1 = reinterpret_cast<float*>(ws + c.out1);
   float* o2 = reinterpret_cast<float*>(ws + c.out2);
   float* l1 = reinterpret_cast<float*>(ws + c.lse1);
   float* l2 = reinterpret_cast<float*>(ws + c.lse2);
   const int prefix_tokens = prefix_blocks * block_size;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (pa::launch_cascade_prep(context_lens, num_seqs, prefix_tokens, max_context_len, ints,
-                              ints + 2, ints + 3, st) != hipSuccess)
-    return PA_ERR_HIP;
-  // the shared prefix: every sequence's query as one row over row 0's first blocks;
-  // with several partitions their partials stay in the workspace for the combine
+  // the shared prefix: every sequence's query as one row of a single sequence
+  // over row 0's first blocks, the partition partials left in the workspace
   const int part = resolve_partition(0, 1, num_heads, num_kv_heads, block_size, prefix_tokens,
                                      num_seqs);
   const int n_parts = std::max(1, ceil_div(prefix_tokens, part));
-  rc = multiq_core(o1, q, k_cache, v_cache, block_tables, ints + 2, ints, 1, num_seqs, num_seqs,
-                   num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                   prefix_tokens, scale, 0, dtype, PA_F32, 0, c.mq_bytes ? ws + c.mq : nullptr,
-                   c.mq_bytes, stream, l1, none, /*no_merge=*/1);
+  rc = multiq_core(o1, q, k_cache, v_cache, block_tables, nullptr, nullptr, 1, num_seqs,
+                   num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                   max_blocks_per_seq, prefix_tokens, scale, 0, dtype, PA_F32, 0,
+                   c.mq_bytes ? ws + c.mq : nullptr, c.mq_bytes, stream, l1, none,
+                   /*no_merge=*/1, /*fixed_rows=*/num_seqs);
   if (rc != PA_OK) return rc;
-  const float* p_ml = reinterpret_cast<const float*>(ws + c.mq);
-  const float* p_o = p_ml + partial_ml_floats(num_seqs, num_heads, n_parts);
-  // each sequence's own tail: its table from entry prefix_blocks on (same row stride)
-  rc = decode_core(o2, q, k_cache, v_cache, block_tables + prefix_blocks, ints + 3, num_seqs,
+  // each sequence's own tail: its table from entry prefix_blocks on (same row
+  // stride), its length less the prefix; with the balanced split the pieces
+  // stay in the workspace for the fold
+  pa::AttnArgs ta{};
+  rc = decode_core(o2, q, k_cache, v_cache, block_tables + prefix_blocks, context_lens, num_seqs,
                    num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                    max_context_len - prefix_tokens, scale, dtype, PA_F32, 0,
-                   c.dec_bytes ? ws + c.dec : nullptr, c.dec_bytes, stream, l2, none);
+                   c.dec_bytes ? ws + c.dec : nullptr, c.dec_bytes, stream, l2, none, 1.f, false,
+                   prefix_tokens, /*split_no_merge=*/true, &ta);
   if (rc != PA_OK) return rc;
-  hipError_t e = pa::launch_cascade_combine(out, p_ml, p_o, n_parts, n_parts, o1, l1, o2, l2,
-                                            num_seqs, num_heads, head_dim, out_dtype, st);
+  pa::CascadeFold f{};
+  f.out = out;
+  f.out_dtype = out_dtype;
+  f.num_seqs = num_seqs;
+  f.num_heads = num_heads;
+  f.num_kv_heads = num_kv_heads;
+  f.group = num_heads / num_kv_heads;
+  f.context_lens = context_lens;
+  f.prefix_tokens = prefix_tokens;
+  f.tail_max_len = max_context_len - prefix_tokens;
+  f.p_ml = reinterpret_cast<const float*>(ws + c.mq);
+  f.p_o = f.p_ml + partial_ml_floats(num_seqs, num_heads, n_parts);
+  f.n_parts = n_parts;
+  f.o1 = o1;
+  f.lse1 = l1;
+  f.plan = ta.plan;
+  f.t_ml = ta.ws_ml;
+  f.t_o = ta.ws_o;
+  f.o2 = o2;
+  f.lse2 = l2;
+  hipError_t e = pa::launch_cascade_fold(f, head_dim, st);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -465,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
   if (tid == 0) sm_pre[0] = 0;
   for (int base = 0; base < S; base += kThreads) {
     const int s = base + tid;
-    const int L = s < S ? min(max(a.context_lens[s], 0), a.max_context_len) : 0;
+    const int L = s < S ? min(max(a.context_lens[s] - a.len_offset, 0), a.max_context_len) : 0;
     int v = (L + B - 1) / B;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
   const size_t blk_bytes = (size_t)Hk * W::kSliceBytes;
   const ConstI32Ptr lens = as_const(a.context_lens);
   while (f < f_end) {
-    const int L = min(max(lens[s], 0), a.max_context_len);
+    const int L = min(max(lens[s] - a.len_offset, 0), a.max_context_len);
     const int n_here = min(nb - j, f_end - f);
     const size_t head0 = (size_t)s * H + (size_t)g * G;
     w.load_q(a.q, head0, G, a.scale_log2);
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnArgs a) {
   const int s = blockIdx.y;
   const int g = hq / G, h = hq - g * G;
   const ConstI32Ptr plan = as_const(a.plan);
-  const int Lraw = as_const(a.context_lens)[s];
+  const int Lraw = as_const(a.context_lens)[s] - a.len_offset;
   const int chunk = plan[0];
   const int p0 = plan[2 + s], p1 = plan[3 + s];
   const size_t oidx = ((size_t)s * H + hq) * D + d0;
@@ -663,18 +663,21 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const AttnAr
   // Decode: blockIdx.z is the sequence and its one query row.  Per-row mode
   // (multi-token queries without MFMA): blockIdx.z = s * max_q_len + i is row i
   // of sequence s, which sees the first L_s - n_s + i + 1 keys when causal.
+  // (fixed_rows: one sequence of fixed_rows rows and length max_context_len)
+  const bool rows_mode = a.q_offsets || a.fixed_rows > 0;
   int s = blockIdx.z, qrow = blockIdx.z, i = 0, n = 1;
-  if (a.q_offsets) {
+  if (rows_mode) {
     s = blockIdx.z / a.max_q_len;
     i = blockIdx.z % a.max_q_len;
-    const int q0 = a.q_offsets[s];
-    n = a.q_offsets[s + 1] - q0;
+    const int q0 = a.fixed_rows > 0 ? 0 : a.q_offsets[s];
+    n = a.fixed_rows > 0 ? a.fixed_rows : a.q_offsets[s + 1] - q0;
     if (i >= n) return;
     qrow = q0 + i;
   }
   // context_lens is read only once s is known (blockIdx.z may exceed S)
-  int L = min(max(a.context_lens[s], 0), a.max_context_len);
-  if (a.q_offsets && a.causal) L = max(0, min(L, L - n + i + 1));
+  int L = a.fixed_rows > 0 ? a.max_context_len
+                           : min(max(a.context_lens[s] - a.len_offset, 0), a.max_context_len);
+  if (rows_mode && a.causal) L = max(0, min(L, L - n + i + 1));
   const int n_parts = (L + a.part - 1) / a.part;
 
   const int tid = threadIdx.x;
@@ -765,7 +768,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
   const int hq = c / kChunks, d0 = (c % kChunks) * 4;
   const int s = blockIdx.z;
   size_t row = s;
-  int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  int L = min(max(a.context_lens[s] - a.len_offset, 0), a.max_context_len);
   if (a.q_offsets) {  // multi-token queries: blockIdx.y = row within the sequence
     const int q0 = a.q_offsets[s], n = a.q_offsets[s + 1] - q0;
     const int i = blockIdx.y;
@@ -854,18 +857,18 @@ static hipError_t launch_decode_t(int num_seqs, const AttnArgs& a, hipStream_t s
     const size_t smem = ((size_t)num_seqs + 1) * sizeof(int);
     hipError_t e = launch_main(decode_split_kernel<DT, D, B, GP>, dim3(a.split_workgroups),
                                dim3(kThreads), smem, st, ev, a);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.no_merge) return e;
     const int chunks = a.num_heads * D / 4;   // 4-dim chunks of a sequence's outputs
     hipLaunchKernelGGL((split_merge_kernel<D>), dim3((chunks + 255) / 256, num_seqs), dim3(256), 0,
                        st, a);
     return hipGetLastError();
   }
   // per-row mode launches one grid row per (sequence, query row) slot
-  const int rows = a.q_offsets ? num_seqs * a.max_q_len : num_seqs;
+  const int rows = (a.q_offsets || a.fixed_rows > 0) ? num_seqs * a.max_q_len : num_seqs;
   dim3 grid(a.max_parts, a.num_kv_heads, rows);
   hipError_t e = launch_main(decode_partition_kernel<DT, D, B, GP>, grid, dim3(kThreads), 0, st,
                              ev, a);
-  if (e != hipSuccess || a.max_parts <= 1) return e;
+  if (e != hipSuccess || a.max_parts <= 1 || a.no_merge) return e;
   return launch_merge(D, num_seqs, a, st);
 }
 

@@ -62,9 +62,16 @@ struct AttnArgs {
   float* lse;
   int chunk_blocks;          // items per wave (0: split evenly over the launch)
   int split_workgroups;      // workgroups launched
-  // multi-token calls: leave the partition partials in the workspace for the
-  // caller's own merge instead of launching merge_kernel
+  // leave the partials in the workspace for the caller's own merge instead of
+  // launching merge_kernel (multi-token calls) or split_merge_kernel (decode)
   int no_merge;
+  // subtracted from every context length before it is clamped to
+  // [0, max_context_len] (the tails of a shared-prefix decode)
+  int len_offset;
+  // > 0: one sequence whose query rows are 0 .. fixed_rows - 1 and whose
+  // length is max_context_len; q_offsets and context_lens are not read (the
+  // prefix pass of a shared-prefix decode)
+  int fixed_rows;
 };
 
 // Optional events recorded right around a call's main kernel (profiling aid).
@@ -99,17 +106,24 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
                               int elem_bytes, hipStream_t stream);
 
-hipError_t launch_cascade_prep(const int32_t* context_lens, int num_seqs, int prefix_tokens,
-                               int max_context_len, int32_t* q_offsets, int32_t* prefix_len,
-                               int32_t* tail_lens, hipStream_t stream);
-
 // Final rows of the shared-prefix decode: the prefix pass's n_parts partition
 // partials (or, with one partition, its normalized output o1 and lse1) and the
-// tail pass's normalized output o2 and lse2, combined by log-sum-exp.
-hipError_t launch_cascade_combine(void* out, const float* ws_ml, const float* ws_o, int max_parts,
-                                  int n_parts, const float* o1, const float* lse1, const float* o2,
-                                  const float* lse2, int num_seqs, int num_heads, int head_dim,
-                                  int out_dtype, hipStream_t stream);
+// tail pass's output -- with the balanced split (plan != nullptr), the pieces
+// it left in its workspace, or o2 and lse2 for a (sequence, KV head) that one
+// wave covered; otherwise o2 and lse2 -- combined by log-sum-exp.
+struct CascadeFold {
+  void* out;
+  int out_dtype, num_seqs, num_heads, num_kv_heads, group;
+  const int32_t* context_lens;
+  int prefix_tokens, tail_max_len;
+  const float *p_ml, *p_o;   // prefix partials [rows][H][n_parts][2], [..][D]
+  int n_parts;
+  const float *o1, *lse1;
+  const int* plan;           // tail split plan, or nullptr
+  const float *t_ml, *t_o;   // tail pieces
+  const float *o2, *lse2;
+};
+hipError_t launch_cascade_fold(const CascadeFold& f, int head_dim, hipStream_t stream);
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int workgroups,
                               int nontemporal, hipStream_t stream);

@@ -137,11 +137,13 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
   const int p = wg % a.max_parts;
   wg /= a.max_parts;
   const int g = wg % Hk, s = wg / Hk;
-  const int q0 = a.q_offsets[s], n = a.q_offsets[s + 1] - q0;
+  const int q0 = a.fixed_rows > 0 ? 0 : a.q_offsets[s];
+  const int n = a.fixed_rows > 0 ? a.fixed_rows : a.q_offsets[s + 1] - q0;
   const int n_rows = n * G;
   const int wg_row0 = (ROWS ? ux * kWaves : ux) * 32;
   if (wg_row0 >= n_rows) return;       // workgroup-uniform
-  const int L = min(max(a.context_lens[s], 0), a.max_context_len);
+  const int L = a.fixed_rows > 0 ? a.max_context_len
+                                 : min(max(a.context_lens[s], 0), a.max_context_len);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

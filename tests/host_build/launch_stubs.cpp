@@ -29,15 +29,7 @@ hipError_t launch_copy_blocks(void*, void*, const int32_t*, int, int, int, int, 
                               hipStream_t) {
   return hipErrorNoDevice;
 }
-hipError_t launch_cascade_prep(const int32_t*, int, int, int, int32_t*, int32_t*, int32_t*,
-                               hipStream_t) {
-  return hipErrorNoDevice;
-}
-hipError_t launch_cascade_combine(void*, const float*, const float*, int, int, const float*,
-                                  const float*, const float*, const float*, int, int, int, int,
-                                  hipStream_t) {
-  return hipErrorNoDevice;
-}
+hipError_t launch_cascade_fold(const CascadeFold&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_stream_read(const void*, size_t, unsigned*, int, int, hipStream_t) {
   return hipErrorNoDevice;
 }
