@@ -80,8 +80,10 @@ struct SplitPlan {
   int workgroups = 0;
 };
 
+// items of the balanced split at most: every (sequence, KV head) costs its
+// blocks plus kSegItems
 int64_t split_bound(int num_seqs, int num_kv_heads, int block_size, int max_context_len) {
-  return (int64_t)num_seqs * num_kv_heads * ceil_div(max_context_len, block_size);
+  return (int64_t)num_seqs * num_kv_heads * (ceil_div(max_context_len, block_size) + pa::kSegItems);
 }
 
 SplitPlan plan_split(int num_seqs, int num_kv_heads, int block_size, int max_context_len,

@@ -101,9 +101,9 @@ __global__ __launch_bounds__(256) void cascade_fold_kernel(const CascadeFold f) 
 
   // the tail part
   if (Lt > 0) {
-    const int nb = p1 - p0;
-    const int a0 = Hk * p0 + g * nb;
-    const int w0 = f.plan ? a0 / chunk : 0, w1 = f.plan ? (a0 + nb - 1) / chunk : 0;
+    const int c = p1 - p0;   // (s, g)'s items: its own cost, then its blocks
+    const int a0 = Hk * p0 + g * c;
+    const int w0 = f.plan ? (a0 + kSegItems) / chunk : 0, w1 = f.plan ? (a0 + c - 1) / chunk : 0;
     if (w0 == w1) {   // written as a normalized output with its log-sum-exp
       float pm[kBatch], pl[kBatch];
       float4 pv[kBatch];

@@ -26,9 +26,10 @@
 // valid token free of inf - inf.
 //
 // Two ways to cut the work into waves:
-//  * split (decode default): every (sequence, KV head, block) item is numbered
-//    in one list and each resident wave takes an equal contiguous chunk, so all
-//    waves finish together whatever the mix of context lengths.  A chunk that
+//  * split (decode default): every (sequence, KV head, block) item, with a
+//    fixed cost item per (sequence, KV head), is numbered in one list and each
+//    resident wave takes an equal contiguous chunk, so all waves finish
+//    together whatever the mix of context lengths.  A chunk that
 //    covers a whole (sequence, KV head) writes the output; pieces of a longer
 //    one write (max, sum, unnormalized output) partials that split_merge_kernel
 //    combines by log-sum-exp.
@@ -444,35 +445,46 @@ struct DecodeWave {
 // ---------------------------------------------------------------------------
 // split kernel: equal chunks of the flattened (sequence, KV head, block) list
 // ---------------------------------------------------------------------------
-// Items are numbered f = Hk pre[s] + g nb[s] + j (nb[s] = blocks of sequence
-// s, pre its exclusive prefix sum); wave w takes f in [w chunk, (w+1) chunk).
-// Workgroup 0 stores the plan for the merge: plan[0] = chunk, plan[1] = total
-// items, plan[2 ..] = pre[0 .. S].
+// Each (sequence, KV head) with nb[s] > 0 blocks is c[s] = kSegItems + nb[s]
+// items: its fixed cost (starting a segment: the query, the first block's
+// latency, the final stores), then its blocks.  Items are numbered
+// f = Hk pre[s] + g c[s] + k (pre: exclusive prefix sum of c); wave w takes f
+// in [w chunk, (w+1) chunk), and item k >= kSegItems is block k - kSegItems.
+// A length mix with many short segments would otherwise leave the waves that
+// draw them far behind the others.  Workgroup 0 stores the plan for the
+// merge: plan[0] = chunk, plan[1] = total items, plan[2 ..] = pre[0 .. S].
 template <int DT, int D, int B, int GP>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a) {
   using W = DecodeWave<DT, D, B, GP>;
-  extern __shared__ int sm_pre[];   // [S + 1] prefix sums of blocks per sequence
-  __shared__ int sm_wsum[kWaves];
+  extern __shared__ int sm_pre[];   // [S + 1] prefix sums of items per sequence
+  __shared__ int sm_wsum[kWaves], sm_wne[kWaves];
   const int S = a.num_seqs, H = a.num_heads, Hk = a.num_kv_heads, G = a.group;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int X = kSegItems;
 
-  // Block counts per sequence and their prefix sums, 256 sequences per round:
-  // an inclusive scan inside each wave (shuffles), then the wave totals
-  // through LDS (two barriers per round).
-  int carry = 0;
+  // Items per sequence (per KV head: its blocks plus X if it has any) and
+  // their prefix sums, 256 sequences per round: an inclusive scan inside each
+  // wave (shuffles), then the wave totals through LDS (two barriers per
+  // round).  The non-empty sequences are counted alongside.
+  int carry = 0, nonempty = 0;
   if (tid == 0) sm_pre[0] = 0;
   for (int base = 0; base < S; base += kThreads) {
     const int s = base + tid;
     const int L = s < S ? min(max(a.context_lens[s] - a.len_offset, 0), a.max_context_len) : 0;
-    int v = (L + B - 1) / B;
+    const int nbs = (L + B - 1) / B;
+    int v = nbs > 0 ? nbs + X : 0;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int t = __shfl_up(v, off, 64);
       v += lane >= off ? t : 0;
     }
-    if (lane == 63) sm_wsum[wave] = v;
+    const uint64_t ne = __builtin_amdgcn_ballot_w64(nbs > 0);   // (all lanes take part)
+    if (lane == 63) {
+      sm_wsum[wave] = v;
+      sm_wne[wave] = __builtin_popcountll(ne);
+    }
     __syncthreads();
     int before = carry;
 #pragma unroll
@@ -480,6 +492,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
       const int t = sm_wsum[w];
       before += w < wave ? t : 0;
       carry += t;
+      nonempty += sm_wne[w];
     }
     if (s < S) sm_pre[s + 1] = before + v;
     __syncthreads();
@@ -488,7 +501,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
   // More table entries than pool blocks means some block serves several
   // sequences (a shared prefix): then K/V lines are worth keeping in the
   // caches.  Otherwise every block is (almost surely) read once: stream it.
-  const bool stream = total / Hk <= a.pool_blocks;
+  const int entries = __builtin_amdgcn_readfirstlane(sm_pre[S] - X * nonempty);
+  const bool stream = entries <= a.pool_blocks;
   const int nwaves = gridDim.x * kWaves;
   const int chunk = a.chunk_blocks > 0 ? a.chunk_blocks : max(1, (total + nwaves - 1) / nwaves);
   if (blockIdx.x == 0) {
@@ -516,14 +530,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
     else hi = mid - 1;
   }
   int s = lo;
-  int nb = pre_at(s + 1) - pre_at(s);
+  int c = pre_at(s + 1) - pre_at(s);   // items of each KV head of s (> 0)
   const int r0 = f - Hk * pre_at(s);
-  int g = r0 / nb, j = r0 % nb;
+  int g = r0 / c, k = r0 % c;          // k: item within (s, g); its first X are no block
 
   W w(lane);
   const size_t blk_bytes = (size_t)Hk * W::kSliceBytes;
   const ConstI32Ptr lens = as_const(a.context_lens);
   while (f < f_end) {
+    if (k < X) {                      // the segment's own cost: no block
+      f += X - k;
+      k = X;
+      if (f >= f_end) break;
+    }
+    const int nb = c - X, j = k - X;
     const int L = min(max(lens[s] - a.len_offset, 0), a.max_context_len);
     const int n_here = min(nb - j, f_end - f);
     const size_t head0 = (size_t)s * H + (size_t)g * G;
@@ -565,15 +585,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
       }
     }
     f += n_here;
-    j += n_here;
-    if (j == nb && f < f_end) {       // next KV head, or the next non-empty sequence
-      j = 0;
+    k += n_here;
+    if (k == c && f < f_end) {        // next KV head, or the next non-empty sequence
+      k = 0;
       if (++g == Hk) {
         g = 0;
         do {
           ++s;
         } while (pre_at(s + 1) == pre_at(s));
-        nb = pre_at(s + 1) - pre_at(s);
+        c = pre_at(s + 1) - pre_at(s);
       }
     }
   }
@@ -582,9 +602,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const AttnArgs a
 // Merge of the split kernel's pieces for one sequence; thread c owns 4
 // consecutive dims of one query head (16-byte loads of the pieces' partial
 // outputs), so a 256-thread workgroup covers 1,024 of the sequence's H*D
-// outputs.  The items of (s, g) are [a0, a0 + nb) with a0 = Hk pre[s] + g nb,
-// so the waves that covered them are a0 / chunk .. (a0 + nb - 1) / chunk, and
-// wave w left its piece in slot (s Hk + g + w) G + h.  Empty contexts get zero
+// outputs.  The items of (s, g) are [a0, a0 + c) with a0 = Hk pre[s] + g c,
+// its blocks the last c - kSegItems of them, so the waves that covered its
+// blocks are (a0 + kSegItems) / chunk .. (a0 + c - 1) / chunk, and wave w
+// left its piece in slot (s Hk + g + w) G + h.  Empty contexts get zero
 // rows.  The plan, the length and the prefix sums are read together, then the
 // pieces' (max, sum, o) in batches of independent loads.
 template <int D>
@@ -607,9 +628,12 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnArgs a) {
     if (a.lse && d0 == 0) a.lse[(size_t)s * H + hq] = kNegInf;
     return;
   }
-  const int nb = p1 - p0;
-  const int a0 = Hk * p0 + g * nb;
-  const int w0 = a0 / chunk, w1 = (a0 + nb - 1) / chunk;
+  // (s, g) holds items [a0, a0 + items): its own cost first, then its
+  // blocks, which waves (a0 + kSegItems) / chunk .. (a0 + items - 1) / chunk
+  // covered
+  const int items = p1 - p0;
+  const int a0 = Hk * p0 + g * items;
+  const int w0 = (a0 + kSegItems) / chunk, w1 = (a0 + items - 1) / chunk;
   if (w0 == w1) return;               // written by its one wave
   const size_t base = (size_t)s * Hk + g;
   constexpr int kBatch = 8;

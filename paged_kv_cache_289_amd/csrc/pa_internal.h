@@ -29,6 +29,13 @@ inline bool multiq_rows_mode(int max_q_len, int group) {
 // live in LDS), and most waves it launches (the workspace is sized for this).
 constexpr int kMaxSplitSeqs = 8192;
 constexpr int kMaxSplitWaves = 8192;
+// The split prices every (sequence, KV head) segment at its blocks plus this
+// many items: a wave that starts a segment loads its query and waits for its
+// first block with nothing else in flight, and stores its result at the end.
+#ifndef PA_SEG_ITEMS
+#define PA_SEG_ITEMS 4
+#endif
+constexpr int kSegItems = PA_SEG_ITEMS;
 
 // Arguments of the decode / multi-query partial kernels and of the merge.
 struct AttnArgs {

@@ -154,15 +154,19 @@ def test_gather_and_check_reject_bad_arguments_on_host():
 
 def test_workspace_size_formula():
     # Decode, 64 sequences x 8 KV heads (G = 4), head_dim 128, contexts up to 4096 in
-    # 16-token blocks, 256-token pieces: at most 64*8*256 = 131072 items in pieces of 16
-    # blocks -> 8192 waves; the plan (2 + 65 int32, on 256 bytes), then fp32 (max, sum)
-    # and outputs for (64*8 + 8192) slots x 4 heads, each region on a 256-byte boundary.
+    # 16-token blocks, 256-token pieces: each (sequence, KV head) is at most 256 block
+    # items plus its 4 fixed-cost items, 64*8*260 = 133120 items in pieces of 16 ->
+    # 8320 waves; the plan (2 + 65 int32, on 256 bytes), then fp32 (max, sum) and
+    # outputs for (64*8 + 8320) slots x 4 heads, each region on a 256-byte boundary.
+    seg = 4
     n = ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 256)
-    slots = 64 * 8 + 8192
+    slots = 64 * 8 + (64 * 8 * (256 + seg) + 15) // 16
     assert n == 512 + slots * 4 * 2 * 4 + slots * 4 * 128 * 4
     assert (slots * 4 * 2 * 4) % 256 == 0
     # default pieces: the launch never exceeds 8192 waves
-    assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 0) == n
+    slots = 64 * 8 + 8192
+    assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 0) == \
+        512 + slots * 4 * 2 * 4 + slots * 4 * 128 * 4
     # multi-token rows whose contexts fit one partition need no workspace
     assert ops.workspace_size(2, 10, 5, 32, 8, 128, 16, 256, 0) == 0
     assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 24) == 0     # rejected
