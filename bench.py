@@ -432,12 +432,17 @@ def main():
     q = dv["q"]
     out = torch.empty(q.shape, dtype=q.dtype, device=dev)
     H, D = st.num_heads, st.head_dim
-    # 0 = the library's choice: balanced split for decode, a partition size for
-    # multi-token queries (reported below)
+    # 0 = the library's choice: balanced split for decode and for multi-token
+    # calls with few rows per KV head, else a partition size (reported below)
     part = a.partition
-    part_used = part or (ops.default_partition(st.num_seqs, st.num_heads, st.num_kv_heads,
-                                               st.block_size, st.max_context_len, st.max_q_len)
-                         if is_multiq else "balanced split")
+    if is_multiq and ops.multiq_uses_split(st.num_seqs, st.max_q_len, st.num_heads,
+                                           st.num_kv_heads, st.head_dim, q.dtype, part):
+        part_used = "balanced split"
+    else:
+        part_used = part or (ops.default_partition(st.num_seqs, st.num_heads, st.num_kv_heads,
+                                                   st.block_size, st.max_context_len,
+                                                   st.max_q_len)
+                             if is_multiq else "balanced split")
     wsb = ops.workspace_size(st.num_seqs, st.total_q, st.max_q_len, H, st.num_kv_heads, D,
                              st.block_size, st.max_context_len, part)
     ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)

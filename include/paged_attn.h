@@ -150,6 +150,13 @@ int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, con
  * context_lens[s] >= n_s); with causal == 0 every row sees all keys.
  * The contraction runs on bf16/fp16 MFMA with fp32 accumulation (dtype PA_F32
  * runs a vector-ALU path).  Other conventions as paged_attn_decode.
+ * Work split: with partition_tokens 0, bf16/f16 calls at head_dim 128 whose
+ * rows fit in at most three 32-row tiles per KV head (max_q_len * num_heads /
+ * num_kv_heads <= 96, max_q_len >= 2) cut the (sequence, KV head, row tile,
+ * 32-key tile) list into equal chunks, one per resident wave, and merge the
+ * pieces of a (sequence, KV head, row tile) that several waves share
+ * (paged_attn_multiq_uses_split says which calls do); other calls use fixed
+ * context partitions of partition_tokens (0: paged_attn_default_partition).
  */
 int paged_attn_multiq(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens,
@@ -203,10 +210,17 @@ int paged_attn_check_inputs(const int32_t* block_tables, const int32_t* context_
 int paged_attn_set_kernel_events(void* start, void* stop);
 
 /* Partition length (tokens) that the library picks when partition_tokens is 0
-   for multi-token queries, or for decode batches above 8192 sequences (other
-   decode calls use the balanced split and no fixed partition). */
+   for multi-token queries that do not take the balanced split, or for decode
+   batches above 8192 sequences (other decode calls use the balanced split and
+   no fixed partition). */
 int paged_attn_default_partition(int num_seqs, int num_heads, int num_kv_heads, int block_size,
                                  int max_context_len, int max_q_len);
+
+/* 1 if paged_attn_multiq with these sizes, dtype and partition_tokens splits
+   its work evenly over the resident waves (the balanced split described at
+   paged_attn_multiq), 0 if it uses fixed context partitions.  Host-only. */
+int paged_attn_multiq_uses_split(int num_seqs, int max_q_len, int num_heads, int num_kv_heads,
+                                 int head_dim, int dtype, int partition_tokens);
 
 /*
  * Decode over a shared prefix.  Same result as paged_attn_decode (same

@@ -139,6 +139,50 @@ void split_workspace_ptrs(void* ws, int num_seqs, int num_heads, int num_kv_head
   a->ws_o = reinterpret_cast<float*>(base + l.o);
 }
 
+// Balanced-split multi-query calls: several query tokens per sequence, rows
+// that fit fewer than four 32-row tiles per KV head (the token layout),
+// head_dim 128, the library's own work split (partition_tokens 0) and a
+// bounded number of (sequence, KV head, row tile) units.  Applies to bf16 and
+// f16; the workspace size covers it whatever the dtype.
+int64_t mq_split_units(int num_seqs, int max_q_len, int num_heads, int num_kv_heads) {
+  const int group = num_heads / num_kv_heads;
+  return (int64_t)num_seqs * num_kv_heads * ceil_div(max_q_len * group, 32);
+}
+
+bool mq_split_shape(int num_seqs, int max_q_len, int num_heads, int num_kv_heads, int head_dim,
+                    int partition_tokens) {
+  if (partition_tokens != 0 || head_dim != 128 || max_q_len < 2 || num_seqs < 1 ||
+      num_seqs > pa::kMaxSplitSeqs || num_kv_heads < 1 || num_heads % num_kv_heads)
+    return false;
+  if (pa::multiq_rows_mode(max_q_len, num_heads / num_kv_heads)) return false;
+  return mq_split_units(num_seqs, max_q_len, num_heads, num_kv_heads) <= pa::kMqMaxSplitUnits;
+}
+
+// Waves of a split launch: one per item at most, kMqMaxSplitWaves at most
+// (fewer where fewer are resident), in whole workgroups.  The workspace is
+// sized for the device-independent bound.
+int mq_split_waves(int64_t units, int max_context_len, int resident) {
+  const int64_t items = units * (ceil_div(max_context_len, 32) + pa::kMqSegItems);
+  const int64_t w =
+      std::max<int64_t>(1, std::min<int64_t>(items, std::min(resident, pa::kMqMaxSplitWaves)));
+  return (int)((w + pa::kWaves - 1) / pa::kWaves * pa::kWaves);
+}
+
+// Its workspace, each region on a 256-byte boundary: the int32 plan
+// [2 + S + 1] that the merge reads, then fp32 (max, sum) pairs and fp32 partial
+// outputs for (units + waves) slots x 32 rows.
+SplitLayout mq_split_layout(int num_seqs, int max_q_len, int num_heads, int num_kv_heads,
+                            int head_dim, int waves) {
+  SplitLayout l;
+  const size_t rows =
+      ((size_t)mq_split_units(num_seqs, max_q_len, num_heads, num_kv_heads) + waves) * 32;
+  l.plan = 0;
+  l.ml = align256((size_t)(3 + num_seqs) * sizeof(int32_t));
+  l.o = l.ml + align256(rows * 2 * sizeof(float));
+  l.total = l.o + rows * (size_t)head_dim * sizeof(float);
+  return l;
+}
+
 // Waves the workspace must allow for when the launch size is not known yet
 // (it depends on the device's CU count and the kernel's occupancy).
 int split_waves_bound(int num_seqs, int num_kv_heads, int block_size, int max_context_len,
@@ -216,6 +260,15 @@ int paged_attn_default_partition(int num_seqs, int num_heads, int num_kv_heads, 
   return part;
 }
 
+int paged_attn_multiq_uses_split(int num_seqs, int max_q_len, int num_heads, int num_kv_heads,
+                                 int head_dim, int dtype, int partition_tokens) {
+  return (dtype == PA_BF16 || dtype == PA_F16) &&
+                 mq_split_shape(num_seqs, max_q_len, num_heads, num_kv_heads, head_dim,
+                                partition_tokens)
+             ? 1
+             : 0;
+}
+
 size_t paged_attn_workspace_size(int num_seqs, int total_q, int max_q_len, int num_heads,
                                  int num_kv_heads, int head_dim, int block_size,
                                  int max_context_len, int partition_tokens) {
@@ -233,7 +286,15 @@ size_t paged_attn_workspace_size(int num_seqs, int total_q, int max_q_len, int n
   const int part = resolve_partition(partition_tokens, num_seqs, num_heads, num_kv_heads,
                                      block_size, max_context_len, max_q_len);
   const int max_parts = ceil_div(max_context_len, part);
-  return workspace_bytes_for(total_q, num_heads, head_dim, max_parts);
+  const size_t parts_bytes = workspace_bytes_for(total_q, num_heads, head_dim, max_parts);
+  if (mq_split_shape(num_seqs, max_q_len, num_heads, num_kv_heads, head_dim, partition_tokens))
+    return std::max(parts_bytes,
+                    mq_split_layout(num_seqs, max_q_len, num_heads, num_kv_heads, head_dim,
+                                    mq_split_waves(mq_split_units(num_seqs, max_q_len, num_heads,
+                                                                  num_kv_heads),
+                                                   max_context_len, pa::kMqMaxSplitWaves))
+                        .total);
+  return parts_bytes;
 }
 
 }  // extern "C"
@@ -403,6 +464,56 @@ int multiq_core(void* out, const void* q, const void* k_cache, const void* v_cac
       (fixed_rows == 0 && (!context_lens || !q_offsets)))
     return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
+
+  if (!no_merge && fixed_rows == 0 &&
+      paged_attn_multiq_uses_split(num_seqs, max_q_len, num_heads, num_kv_heads, head_dim, dtype,
+                                   partition_tokens)) {
+    // balanced split over the resident waves of this device; the workspace is
+    // checked against the device-independent bound before any HIP call
+    const int64_t units = mq_split_units(num_seqs, max_q_len, num_heads, num_kv_heads);
+    if (!workspace || !aligned16(workspace) ||
+        workspace_bytes <
+            mq_split_layout(num_seqs, max_q_len, num_heads, num_kv_heads, head_dim,
+                            mq_split_waves(units, max_context_len, pa::kMqMaxSplitWaves))
+                .total)
+      return PA_ERR_WORKSPACE;
+    const int resident = device_cus() * pa::multiq_split_workgroups_per_cu(dtype, block_size) *
+                         pa::kWaves;
+    const int waves = mq_split_waves(units, max_context_len, resident);
+    const int workgroups = waves / pa::kWaves;
+    const SplitLayout l = mq_split_layout(num_seqs, max_q_len, num_heads, num_kv_heads, head_dim,
+                                          waves);
+    pa::AttnArgs a{};
+    char* wsb = static_cast<char*>(workspace);
+    a.plan = reinterpret_cast<int*>(wsb + l.plan);
+    a.ws_ml = reinterpret_cast<float*>(wsb + l.ml);
+    a.ws_o = reinterpret_cast<float*>(wsb + l.o);
+    a.split_workgroups = workgroups;
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.q_offsets = q_offsets;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_heads / num_kv_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.pool_blocks = num_blocks;
+    a.max_context_len = max_context_len;
+    a.max_q_len = max_q_len;
+    a.causal = causal ? 1 : 0;
+    a.out_dtype = out_dtype;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out_scale = 1.f;
+    a.lse = lse;
+    hipError_t e = pa::launch_multiq(dtype, head_dim, block_size, a.group, num_seqs, a,
+                                     static_cast<hipStream_t>(stream), ev);
+    if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+  }
 
   const int part = resolve_partition(partition_tokens, num_seqs, num_heads, num_kv_heads,
                                      block_size, max_context_len, max_q_len);

@@ -36,6 +36,16 @@ constexpr int kMaxSplitWaves = 8192;
 #define PA_SEG_ITEMS 4
 #endif
 constexpr int kSegItems = PA_SEG_ITEMS;
+// Balanced-split multi-query calls (few query rows per KV head, head_dim
+// 128): the fixed cost per (sequence, KV head, row tile) in 32-token tiles, the
+// most waves launched and the most units (sequence x KV head x row tile) they
+// take (the workspace holds a 32-row piece per unit and per wave).
+#ifndef PA_MQ_SEG_ITEMS
+#define PA_MQ_SEG_ITEMS 2
+#endif
+constexpr int kMqSegItems = PA_MQ_SEG_ITEMS;
+constexpr int kMqMaxSplitWaves = 4096;
+constexpr int kMqMaxSplitUnits = 16384;
 
 // Arguments of the decode / multi-query partial kernels and of the merge.
 struct AttnArgs {
@@ -62,8 +72,8 @@ struct AttnArgs {
   int out_dtype;
   float scale_log2;          // scale * log2(e): scores are kept in log2 units
   float out_scale;           // factor on every final output (1, or the V scale of 8-bit caches)
-  // balanced-split decode (plan != nullptr)
-  int* plan;                 // [2 + S + 1]: chunk, total items, block prefix sums
+  // balanced split, decode or multi-query (plan != nullptr)
+  int* plan;                 // [2 + S + 1]: chunk, total items, item prefix sums
   // optional: per (row, query head) log-sum-exp of the scores in log2 units,
   // m + log2(l) (-inf for a row with no visible key), written with the output
   float* lse;
@@ -92,6 +102,7 @@ hipError_t launch_decode(int dtype, int head_dim, int block_size, int group, int
 
 // Resident workgroups per CU of the split decode kernel for this configuration.
 int split_workgroups_per_cu(int dtype, int head_dim, int block_size, int group);
+int multiq_split_workgroups_per_cu(int dtype, int block_size);
 
 hipError_t launch_multiq(int dtype, int head_dim, int block_size, int group, int num_seqs,
                          const AttnArgs& a, hipStream_t stream, const KernelEvents& ev);

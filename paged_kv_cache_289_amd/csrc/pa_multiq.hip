@@ -18,17 +18,23 @@
 //                    V at dim 32b + l % 32 for exactly the tokens whose
 //                    probabilities the lane holds, in the same order (the
 //                    contraction order over a tile's tokens is free, as long
-//                    as both operands share it).  With K/V staged in LDS
-//                    (rows layout below) two LDS transpose reads
-//                    (ds_read_b64_tr_b16) give it per 16-token step; with
-//                    K/V loaded straight into registers (token layout) an
-//                    MFMA of V with an identity puts V into that layout.
+//                    as both operands share it).  With V staged in LDS
+//                    (rows layout, and the token layout at head_dim 128) two
+//                    LDS transpose reads (ds_read_b64_tr_b16) give it per
+//                    16-token step; with V loaded straight into registers
+//                    (token layout at head_dim 64) an MFMA of V with an
+//                    identity puts V into that layout.
 //
-// The four waves of a workgroup split the partition's tiles, each keeping its
-// next tile's loads in flight while it computes one; their (max, sum, O)
-// states are merged through LDS, then written as the final output or as a
-// partition partial for merge_kernel.  fp32: every query row runs the decode
-// kernel over its own visible length.
+// Work split, few rows per KV head (token layout): by default (head_dim 128)
+// a balanced split hands every resident wave an equal share of the flattened
+// (sequence, KV head, row tile, key tile) list, and a merge kernel combines
+// the pieces of units that several waves share; with fixed partitions the
+// four waves of a workgroup split one partition's tiles and merge through
+// LDS, then write the final output or a partial for merge_kernel.  Many rows
+// (rows layout): four row tiles per workgroup share each staged K/V tile.
+// fp32: every query row runs the decode kernel over its own visible length.
+#include <atomic>
+
 #include "pa_common.h"
 
 namespace pa {
@@ -90,6 +96,259 @@ __device__ inline uint4 pack8_exact(const f32x16_t& x, int base) {
 
 // token offset (within a 32-token tile) of C-layout register v in lane half hh
 __device__ constexpr int tile_token(int v, int hh) { return 8 * (v / 4) + 4 * hh + (v % 4); }
+
+// S^T = K Q^T of one 32-token tile: lane (m, hh) gets the scores of row m for
+// tokens t0 + tile_token(v, hh)
+template <int DT, int KS>
+__device__ __forceinline__ f32x16_t tile_qk(const uint4 (&kr)[KS], const uint4 (&qv)[KS]) {
+  f32x16_t sc = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) sc = Mma<DT>::mma(kr[ks], qv[ks], sc);
+  return sc;
+}
+
+// Masking and the online softmax of one tile's scores: keys at or past lim
+// (this lane's row) are masked unless the whole tile is visible to every row
+// of the wave (`unmasked`, wave-uniform).  Updates the running (m, l, o) and
+// returns the P^T operands (pb: p rounded or cut to the input dtype, pl: bf16
+// residual).
+template <int DT, int DB>
+__device__ __forceinline__ void tile_softmax(f32x16_t sc, int t0, int hh, bool unmasked, int lim,
+                                             float c, float& m_run, float& l_run,
+                                             f32x16_t (&o)[DB], uint4& pb0, uint4& pb1,
+                                             uint4& pl0, uint4& pl1) {
+  float mx = kNegInf;
+  if (unmasked) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+  } else {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      sc[v] = (t0 + tile_token(v, hh) < lim) ? sc[v] : kNegInf;
+      mx = fmaxf(mx, sc[v]);
+    }
+  }
+  mx = max_halves(mx) * c;   // the row's tile max in log2 units (c > 0)
+  // Lazy rescaling: the running max moves only when a score beats it by
+  // more than kRescaleLog2; otherwise the weights are taken against the
+  // stale max (so they are at most 2^kRescaleLog2) and o, l keep their scale.
+  if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {   // wave-uniform
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+  }
+  float psum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    sc[v] = fast_exp2(__builtin_fmaf(sc[v], c, -m_run));
+    psum += sc[v];
+  }
+  l_run += sum_halves(psum);
+
+  // P^T operands.  bf16 keeps 8 significant bits, too few for the
+  // probabilities at short contexts, so P is split into a head (p with its
+  // low 16 bits cleared, exact) and the residual p - head (exact in fp32,
+  // then rounded to bf16), and both are multiplied: p is carried to about
+  // 2^-16.  f16's 11 bits are used as they are (rounded to nearest).
+  if constexpr (DT == PA_BF16) {
+    f32x16_t res;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      res[v] = sc[v] - __uint_as_float(__float_as_uint(sc[v]) & 0xffff0000u);
+    pb0 = pack8_exact<DT>(sc, 0);
+    pb1 = pack8_exact<DT>(sc, 8);
+    pl0 = pack8<DT>(res, 0);
+    pl1 = pack8<DT>(res, 8);
+  } else {
+    pb0 = pack8<DT>(sc, 0);
+    pb1 = pack8<DT>(sc, 8);
+  }
+}
+
+// O^T += V^T P^T for one 32-dim block from its two 16-token V^T operands
+template <int DT>
+__device__ __forceinline__ void tile_pv(f32x16_t& o, const uint4& va0, const uint4& va1,
+                                        const uint4& pb0, const uint4& pb1, const uint4& pl0,
+                                        const uint4& pl1) {
+  o = Mma<DT>::mma(va0, pb0, o);
+  o = Mma<DT>::mma(va1, pb1, o);
+  if constexpr (DT == PA_BF16) {
+    o = Mma<DT>::mma(va0, pl0, o);
+    o = Mma<DT>::mma(va1, pl1, o);
+  }
+}
+
+// Q^T operand of lane (m, hh): its row's query (token, head) out_row, dims
+// 16 ks + 8 hh .. +7 (zeros for a lane without a row).  A negative scale goes
+// into q's sign bits (exact), so the scores are scaled by a positive c inside
+// the exponent's FMA.
+template <int D>
+__device__ __forceinline__ void load_q_operand(const void* q, size_t out_row, int hh, bool row_ok,
+                                               float scale_log2, uint4 (&qv)[D / 16]) {
+  constexpr int KS = D / 16;
+  const uint4* qp = reinterpret_cast<const uint4*>(q) + (out_row * D + hh * 8) / 8;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qv[ks] = row_ok ? qp[2 * ks] : make_uint4(0, 0, 0, 0);
+  if (scale_log2 < 0.f) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qv[ks].x ^= 0x80008000u; qv[ks].y ^= 0x80008000u;
+      qv[ks].z ^= 0x80008000u; qv[ks].w ^= 0x80008000u;
+    }
+  }
+}
+
+// Token layout at head_dim 128: one wave walks 32-token tiles of one
+// (sequence, KV head) through its own two 8 KiB LDS stages, one for the K tile
+// and one for the V tile.  Both arrive by direct-to-LDS loads: a wave
+// instruction moves four whole token rows (1 KiB, every lane 16 bytes), which
+// keeps each load instruction on eight full 128-byte lines (loading K straight
+// into the operand layout would touch 32 rows per instruction, 32 bytes of
+// each).  Each stage row's 16-byte chunks are permuted (an XOR on the chunk
+// index, see below) so that the operand reads out of LDS hit distinct banks.
+// Tokens at or past L are clamped to the last valid one (their slots may hold
+// anything) and masked in the scores.
+template <int B>
+struct TokenTileWalker {
+  static constexpr int kRowBytes = 256;            // 128 16-bit elements
+  static constexpr int kStageBytes = 32 * kRowBytes;
+  static constexpr int kTileBlocks = 32 / B;
+  static constexpr int KS = 8, DB = 4;
+  const char* kbase;
+  const char* vbase;
+  ConstI32Ptr tblc;   // the sequence's block table
+  int jlast;          // its last block, (L - 1) / B
+  int L, Hk, g, lane;
+
+  // physical block of token t of the tile at t0 (block ids from scalar loads)
+  __device__ __forceinline__ int phys_of(int t0, int t) const {
+    const int jt = t / B - t0 / B;
+    int phys = tblc[min(t0 / B, jlast)];
+#pragma unroll
+    for (int k = 1; k < kTileBlocks; ++k) {
+      const int id = tblc[min(t0 / B + k, jlast)];
+      phys = (jt == k) ? id : phys;
+    }
+    return phys;
+  }
+  __device__ __forceinline__ size_t row_off(int phys, int t) const {
+    return (((size_t)phys * Hk + g) * B + (t % B)) * kRowBytes;
+  }
+  // V stage: 16-byte chunk c of row r sits at position c ^ 4 (r mod 4), which
+  // keeps the transpose reads (four rows by two chunks per 16 lanes) on
+  // distinct banks.
+  // V^T operands for dim block db and 16-token step ks: dim 32 db + m, tokens
+  // 16 ks + 4 hh + (0..3) then 16 ks + 8 + 4 hh + (0..3), the order of the
+  // lane's probabilities.  In a transpose read, lane i of each 16-lane group
+  // addresses row r0 + i / 4 at dims c0 + 4 (i % 4) .. + 3, and lane j
+  // receives dim c0 + j of rows r0 .. r0 + 3.
+  __device__ __forceinline__ void read_vt(const char* stage, uint4 (&va)[DB][2]) const {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 LdsV4;
+    const int hh = lane >> 5;
+    const int rsub = (lane & 15) / 4;
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int off = (lane & 1) * 8;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int r0 = 16 * ks + 4 * hh + rsub, r1 = r0 + 8;
+        const int c = 4 * db + cl;
+        const char* p0 = stage + r0 * kRowBytes + ((c ^ (4 * (r0 & 3))) * 16) + off;
+        const char* p1 = stage + r1 * kRowBytes + ((c ^ (4 * (r1 & 3))) * 16) + off;
+        const auto lo = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                      (LdsV4*)(__attribute__((address_space(3))) char*)p0));
+        const auto hi = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                      (LdsV4*)(__attribute__((address_space(3))) char*)p1));
+        va[db][ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+  }
+
+  // K stage: instruction i: lane l writes stage bytes 1024 i + 16 l, i.e. row
+  // r = 4 i + l / 16 at position l % 16, which holds chunk (l % 16) ^ (r mod 16);
+  // lane (m, hh) then reads chunk 2 ks + hh of row m, its operand for k-step ks
+  // (16 rows of one lane half hit 16 distinct positions: no bank conflict).
+  // NT: the non-temporal hint.
+  template <bool NT>
+  __device__ __forceinline__ void load_k(int t0, char* stage) const {
+    const int krow = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + krow;
+      const int t = min(t0 + r, L - 1);
+      const char* src = kbase + row_off(phys_of(t0, t), t) + (((lane & 15) ^ (r & 15)) * 16);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(stage + 1024 * i),
+                                       16, 0, NT ? kCpolNt : 0);
+    }
+  }
+  __device__ __forceinline__ void read_k(const char* stage, uint4 (&kr)[KS]) const {
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const u4v LdsU4;
+    const int m = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cpos = (2 * ks + hh) ^ (m & 15);
+      const u4v x = *(LdsU4*)(__attribute__((address_space(3))) const char*)(stage + m * kRowBytes +
+                                                                              cpos * 16);
+      kr[ks] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+  }
+  // V stage: instruction i: lane l writes row 4 i + l / 16 at position l % 16,
+  // which holds chunk (l % 16) ^ 4 (l / 16)
+  template <bool NT>
+  __device__ __forceinline__ void load_v(int t0, char* stage) const {
+    const int vrow = lane >> 4, vchunk = (lane & 15) ^ (4 * (lane >> 4));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = min(t0 + 4 * i + vrow, L - 1);
+      const char* src = vbase + row_off(phys_of(t0, t), t) + vchunk * 16;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(stage + 1024 * i),
+                                       16, 0, NT ? kCpolNt : 0);
+    }
+  }
+
+  // The tiles t0, t0 + stride, ... below t_end (t0 < t_end, wave-uniform)
+  // into the running (m, l, o); keys at or past lim are masked, and a tile
+  // ending at or before unmask_end (wave-uniform) needs no mask.  Each step
+  // waits for its tile, reads all of its operands out of the stages, and only
+  // then (once those reads are back) loads the next tile into the same stages,
+  // so the loads are in flight for the whole of the tile's compute.
+  template <int DT, bool NT>
+  __device__ __forceinline__ void walk(int t0, int t_end, int stride, const uint4 (&qv)[KS],
+                                       float c, int lim, int unmask_end, char* kst, char* vst,
+                                       f32x16_t (&o)[DB], float& m_run, float& l_run) const {
+    const int hh = lane >> 5;
+    t_end = __builtin_amdgcn_readfirstlane(t_end);
+    load_k<NT>(t0, kst);
+    load_v<NT>(t0, vst);
+    for (;;) {
+      uint4 kr[KS];
+      read_k(kst, kr);
+      uint4 va[DB][2];
+      read_vt(vst, va);
+      const bool more = t0 + stride < t_end;   // wave-uniform
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the stages are read
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        load_k<NT>(t0 + stride, kst);
+        load_v<NT>(t0 + stride, vst);
+      }
+      const f32x16_t sc = tile_qk<DT>(kr, qv);
+      uint4 pb0, pb1, pl0, pl1;
+      tile_softmax<DT>(sc, t0, hh, t0 + 32 <= unmask_end, lim, c, m_run, l_run, o, pb0, pb1, pl0,
+                       pl1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) tile_pv<DT>(o[db], va[db][0], va[db][1], pb0, pb1, pl0, pl1);
+      if (!more) break;
+      t0 += stride;
+    }
+  }
+};
 
 // ROWS = false: one 32-row tile per workgroup; its four waves take
 //   interleaved 32-token tiles of the partition (each staging its own tiles
@@ -181,20 +440,7 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
 
   // Q^T operand: row m = lane % 32, dims 16 ks + 8 hh .. +7
   uint4 qv[KS];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.q) + (out_row * D + hh * 8) / 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qv[ks] = row_ok ? qp[2 * ks] : make_uint4(0, 0, 0, 0);
-    // a negative scale goes into q's sign bits (exact), so the scores are
-    // scaled by a positive c inside the exponent's FMA
-    if (a.scale_log2 < 0.f) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        qv[ks].x ^= 0x80008000u; qv[ks].y ^= 0x80008000u;
-        qv[ks].z ^= 0x80008000u; qv[ks].w ^= 0x80008000u;
-      }
-    }
-  }
+  load_q_operand<D>(a.q, out_row, hh, row_ok, a.scale_log2, qv);
   const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
   // identity operands selecting dims 0..15 and 16..31 of a 32-dim block
   uint4 eye[2];
@@ -271,6 +517,11 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
       sv[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
     }
   };
+  // token layout at head_dim 128: a K stage and a V stage of 32 rows per wave
+  constexpr bool kStaged = !ROWS && D == 128;
+  constexpr int kVTile = 32 * kRowBytes;
+  __shared__ __attribute__((aligned(16))) char sm_kst[kStaged ? kWaves * kVTile : 16];
+  __shared__ __attribute__((aligned(16))) char sm_vst[kStaged ? kWaves * kVTile : 16];
   // rows layout: 32-token tiles per loop step, and two LDS stages of a step each
   constexpr int kTps = 1;
   constexpr int kLdsBytes = ROWS ? 2 * kTps * kStageBytes : 16;   // (only the rows layout stages)
@@ -313,76 +564,15 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
       }
   };
 
-  // S^T = K Q^T of one tile: lane holds tokens t0 + tile_token(v, hh) of its row
-  auto qk_tile = [&](const uint4 (&kr)[KS]) {
-    f32x16_t sc = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sc = M::mma(kr[ks], qv[ks], sc);
-    return sc;
-  };
-  // masking and the online softmax of one tile's scores; returns the P^T
-  // operands (pb: p rounded or cut to the input dtype, pl: bf16 residual)
+  auto qk_tile = [&](const uint4 (&kr)[KS]) { return tile_qk<DT>(kr, qv); };
   auto softmax_scores = [&](int t0, f32x16_t sc, uint4& pb0, uint4& pb1, uint4& pl0,
                             uint4& pl1) {
-    float mx = kNegInf;
-    if (t0 + 32 <= min(l_tile_min, tok_end)) {   // wave-uniform: no key of the tile is masked
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        sc[v] = (t0 + tile_token(v, hh) < lim) ? sc[v] : kNegInf;
-        mx = fmaxf(mx, sc[v]);
-      }
-    }
-    mx = max_halves(mx) * c;   // the row's tile max in log2 units (c > 0)
-    // Lazy rescaling: the running max moves only when a score beats it by
-    // more than kRescaleLog2; otherwise the weights are taken against the
-    // stale max (so they are at most 2^kRescaleLog2) and o, l keep their scale.
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {   // wave-uniform
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      sc[v] = fast_exp2(__builtin_fmaf(sc[v], c, -m_run));
-      psum += sc[v];
-    }
-    l_run += sum_halves(psum);
-
-    // P^T operands.  bf16 keeps 8 significant bits, too few for the
-    // probabilities at short contexts, so P is split into a head (p with its
-    // low 16 bits cleared, exact) and the residual p - head (exact in fp32,
-    // then rounded to bf16), and both are multiplied: p is carried to about
-    // 2^-16.  f16's 11 bits are used as they are (rounded to nearest).
-    if constexpr (DT == PA_BF16) {
-      f32x16_t res;
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        res[v] = sc[v] - __uint_as_float(__float_as_uint(sc[v]) & 0xffff0000u);
-      pb0 = pack8_exact<DT>(sc, 0);
-      pb1 = pack8_exact<DT>(sc, 8);
-      pl0 = pack8<DT>(res, 0);
-      pl1 = pack8<DT>(res, 8);
-    } else {
-      pb0 = pack8<DT>(sc, 0);
-      pb1 = pack8<DT>(sc, 8);
-    }
+    tile_softmax<DT>(sc, t0, hh, t0 + 32 <= min(l_tile_min, tok_end), lim, c, m_run, l_run, o,
+                     pb0, pb1, pl0, pl1);
   };
-  // O^T += V^T P^T for dim block db from its two 16-token V^T operands
   auto pv_block = [&](int db, const uint4& va0, const uint4& va1, const uint4& pb0,
                       const uint4& pb1, const uint4& pl0, const uint4& pl1) {
-    o[db] = M::mma(va0, pb0, o[db]);
-    o[db] = M::mma(va1, pb1, o[db]);
-    if constexpr (DT == PA_BF16) {
-      o[db] = M::mma(va0, pl0, o[db]);
-      o[db] = M::mma(va1, pl1, o[db]);
-    }
+    tile_pv<DT>(o[db], va0, va1, pb0, pb1, pl0, pl1);
   };
   // token layout: V rows in registers (token mcol) -> V^T through the identity
   auto compute_tile = [&](int t0, const uint4 (&kr)[KS], const uint4 (&vr)[KS]) {
@@ -448,9 +638,18 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
       t0 += kStep;
     }
     compute_step(t0, sm_kv + buf * kTps * kStageBytes);
+  } else if constexpr (kStaged) {
+    // Each wave takes tiles tok0 + 32 wave, + 32 kWaves, ... through its own
+    // K and V stages (cached loads: partitions of one sequence may share lines)
+    const int t0 = tok0 + 32 * wave;
+    if (t0 < tok_end) {
+      const TokenTileWalker<B> w{kbase, vbase, tblc, jlast, L, Hk, g, lane};
+      w.template walk<DT, false>(t0, tok_end, 32 * kWaves, qv, c, lim, min(l_tile_min, tok_end),
+                                 sm_kst + wave * kVTile, sm_vst + wave * kVTile, o, m_run, l_run);
+    }
   } else {
-    // Each wave takes tiles tok0 + 32 wave, + 32 kWaves, ... and loads them
-    // straight into registers in the operand layout (lane (mcol, hh) reads
+    // (head_dim 64) Each wave takes tiles tok0 + 32 wave, + 32 kWaves, ...
+    // and loads them straight into registers in the operand layout (lane (mcol, hh) reads
     // token t0 + mcol, 16 bytes per k-step).  Two register buffers: the next
     // tile's loads are issued (K, then V, before any of the compute) and stay
     // in flight while a tile is computed; the last tile issues nothing, so
@@ -500,8 +699,13 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
 
   if constexpr (!ROWS) {
     // merge the waves' states through LDS, one wave at a time, into wave 0
-    __shared__ float sm_o[32][D + 4];
+    // (at head_dim 128 in the waves' K stages, once every wave is past them)
+    typedef float MergeO[32][D + 4];
+    __shared__ float sm_o_own[kStaged ? 1 : 32][kStaged ? 1 : D + 4];
     __shared__ float sm_m[32], sm_l[32];
+    static_assert(!kStaged || sizeof(MergeO) <= kWaves * kVTile, "merge area");
+    if constexpr (kStaged) __syncthreads();
+    MergeO& sm_o = *reinterpret_cast<MergeO*>(kStaged ? (void*)sm_kst : (void*)sm_o_own);
     for (int w = 1; w < kWaves; ++w) {
       if (wave == w) {
 #pragma unroll
@@ -559,11 +763,12 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
   }
 }
 
-// The two layouts as kernels.  The rows layout fits two waves per SIMD
-// (it holds one staged chunk per thread instead of two register tiles per
-// wave), which lets one wave's softmax overlap the other's matrix products.
+// The two layouts as kernels, both at two waves per SIMD, which lets one
+// wave's softmax and loads overlap the other's matrix products.  (The rows
+// layout holds one staged chunk per thread; the token layout at head_dim 128
+// keeps only K in registers and stages V in LDS.)
 template <int DT, int D, int B>
-__global__ __launch_bounds__(kThreads) void multiq_mfma_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void multiq_mfma_kernel(const AttnArgs a) {
   multiq_mfma_body<DT, D, B, false>(a);
 }
 
@@ -572,11 +777,320 @@ __global__ __launch_bounds__(kThreads, 2) void multiq_mfma_rows_kernel(const Att
   multiq_mfma_body<DT, D, B, true>(a);
 }
 
+// ---------------------------------------------------------------------------
+// balanced split (token layout, head_dim 128)
+// ---------------------------------------------------------------------------
+// Units are (sequence s, KV head g, row tile rt): R_s = ceil(n_s G / 32) row
+// tiles per KV head.  Each unit of a sequence with n_s > 0 rows and L_s > 0
+// keys costs c_s = nt_s + kMqSegItems items: its nt_s = ceil(L_s / 32) key
+// tiles plus a fixed cost (the query load, the first tile's latency, the
+// stores).  Items are numbered f = pre[s] + (g R_s + rt) c_s + k (pre:
+// exclusive prefix sums of Hk R_s c_s); wave w takes f in [w chunk,
+// (w + 1) chunk), item k >= kMqSegItems being key tile k - kMqSegItems.  So
+// every wave does the same work whatever the mix of context lengths, with no
+// partition size to choose.  A wave that covers all of a unit's tiles writes
+// its rows' outputs; otherwise it leaves its piece (max, sum, unnormalised O
+// of the unit's rows) in slot V + w, V = (s Hk + g) Rmax + rt, which
+// mq_split_merge_kernel combines.  The waves of a workgroup are independent
+// (each has its own K and V stages in LDS).  Workgroup 0 stores the plan for the
+// merge: plan[0] = chunk, plan[1] = total items, plan[2 ..] = pre[0 .. S].
+struct MqSeqShape {
+  int L, n, R, nt;   // keys, rows (tokens), row tiles, key tiles (R = nt = 0: no work)
+};
+__device__ __forceinline__ MqSeqShape mq_seq_shape(const AttnArgs& a, ConstI32Ptr lens,
+                                                   ConstI32Ptr qoff, int s) {
+  MqSeqShape r;
+  r.L = min(max(lens[s], 0), a.max_context_len);
+  r.n = min(max(qoff[s + 1] - qoff[s], 0), a.max_q_len);
+  r.R = (r.n * a.group + 31) / 32;
+  r.nt = (r.L + 31) / 32;
+  if (r.R == 0 || r.nt == 0) r.R = r.nt = 0;
+  return r;
+}
+
+// One wave's share of the split: items [f, f_end), starting r0 items into
+// sequence s (NT: the loads carry the non-temporal hint).
+template <int DT, int B, bool NT>
+__device__ __forceinline__ void mq_split_wave(const AttnArgs& a, int s, int r0, int f, int f_end,
+                                              int wid, char* st0, char* st1) {
+  using Wk = TokenTileWalker<B>;
+  constexpr int D = 128, KS = Wk::KS, DB = Wk::DB, X = kMqSegItems;
+  const int H = a.num_heads, Hk = a.num_kv_heads, G = a.group;
+  const int Rmax = (a.max_q_len * G + 31) / 32;
+  const int lane = threadIdx.x & 63;
+  const ConstI32Ptr lens = as_const(a.context_lens), qoff = as_const(a.q_offsets);
+  MqSeqShape sh = mq_seq_shape(a, lens, qoff, s);
+  int c = sh.nt + X;                   // items of each unit of s
+  int ui = r0 / c, k = r0 % c;
+  int g = ui / sh.R, rt = ui % sh.R;
+  const int hh = lane >> 5, mcol = lane & 31;
+  const float cs = fmaxf(fabsf(a.scale_log2), 1e-30f);
+  const char* kbase = static_cast<const char*>(a.k_cache);
+  const char* vbase = static_cast<const char*>(a.v_cache);
+
+  while (f < f_end) {
+    if (k < X) {                       // the unit's own cost: no tile
+      f += X - k;
+      k = X;
+      if (f >= f_end) break;
+    }
+    const int j = k - X;               // first key tile of this piece
+    const int n_here = min(sh.nt - j, f_end - f);
+    const int L = sh.L, n = sh.n;
+    const int n_rows = n * G;
+    const int r = rt * 32 + mcol;
+    const bool row_ok = r < n_rows;
+    const int qi = row_ok ? r / G : 0;
+    const int qh = row_ok ? r % G : 0;
+    auto visible = [&](int i) { return a.causal ? max(0, min(L, L - n + i + 1)) : L; };
+    const int lrow = row_ok ? visible(qi) : 0;
+    const int l_tile_max = visible(min(rt * 32 + 31, n_rows - 1) / G);
+    const int l_tile_min = visible((rt * 32) / G);
+    const size_t out_row = (size_t)(qoff[s] + qi) * H + (size_t)g * G + qh;
+    uint4 qv[KS];
+    load_q_operand<D>(a.q, out_row, hh, row_ok, a.scale_log2, qv);
+    f32x16_t o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
+    float m_run = kMaxInit, l_run = 0.f;
+    const int seg_end = min(32 * (j + n_here), l_tile_max);
+    if (32 * j < seg_end) {            // (a causal row tile may see fewer tiles)
+      const Wk w{kbase, vbase, as_const(a.block_tables + (size_t)s * a.max_blocks_per_seq),
+                 (L - 1) / B, L, Hk, g, lane};
+      w.template walk<DT, NT>(32 * j, seg_end, 32, qv, cs, min(lrow, seg_end),
+                                  min(l_tile_min, seg_end), st0, st1, o, m_run, l_run);
+    }
+    if (j == 0 && n_here == sh.nt) {   // the whole unit: final output
+      if (row_ok) {
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            store_out(a.out, out_row * D + 32 * db + tile_token(v, hh), o[db][v] * inv,
+                      a.out_dtype);
+        if (a.lse && hh == 0) a.lse[out_row] = lse2_of(m_run, l_run);
+      }
+    } else if (row_ok) {               // a piece: partial for the merge
+      const size_t slot = ((size_t)(s * Hk + g) * Rmax + rt + wid) * 32 + mcol;
+      float* po = a.ws_o + slot * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(po + 32 * db + 8 * q4 + 4 * hh) =
+              make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
+      if (hh == 0) {
+        a.ws_ml[2 * slot] = m_run;
+        a.ws_ml[2 * slot + 1] = l_run;
+      }
+    }
+    f += n_here;
+    k += n_here;
+    if (k == c && f < f_end) {         // next row tile, KV head, or non-empty sequence
+      k = 0;
+      if (++rt == sh.R) {
+        rt = 0;
+        if (++g == Hk) {
+          g = 0;
+          do {
+            ++s;
+            sh = mq_seq_shape(a, lens, qoff, s);
+          } while (sh.R == 0 && s + 1 < a.num_seqs);
+          c = sh.nt + X;
+        }
+      }
+    }
+  }}
+
+template <int DT, int B>
+__global__ __launch_bounds__(kThreads, 2) void multiq_split_kernel(const AttnArgs a) {
+  using Wk = TokenTileWalker<B>;
+  constexpr int X = kMqSegItems;
+  // the waves' K stages, then their V stages; before the walk the same LDS
+  // holds the prefix sums (kMaxSplitSeqs + 1 ints fit)
+  __shared__ __attribute__((aligned(16))) char sm_stage[2 * kWaves * Wk::kStageBytes];
+  __shared__ int sm_wsum[kWaves], sm_went[kWaves];
+  static_assert((kMaxSplitSeqs + 1) * sizeof(int) <= sizeof(sm_stage), "prefix sums fit");
+  int* sm_pre = reinterpret_cast<int*>(sm_stage);
+  const int S = a.num_seqs, Hk = a.num_kv_heads, G = a.group;
+  const int Rmax = (a.max_q_len * G + 31) / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const ConstI32Ptr lens = as_const(a.context_lens), qoff = as_const(a.q_offsets);
+
+  // items per sequence and their prefix sums, 256 sequences per round: an
+  // inclusive scan inside each wave (shuffles), then the wave totals through
+  // LDS (two barriers per round)
+  // The block-table entries that the units read are counted alongside.
+  int carry = 0, entries = 0;
+  if (tid == 0) sm_pre[0] = 0;
+  for (int base = 0; base < S; base += kThreads) {
+    const int s = base + tid;
+    int v = 0, e = 0;
+    if (s < S) {
+      const MqSeqShape sh = mq_seq_shape(a, lens, qoff, s);
+      v = Hk * sh.R * (sh.nt > 0 ? sh.nt + X : 0);
+      e = sh.nt > 0 ? (sh.L + B - 1) / B : 0;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off, 64);
+      v += lane >= off ? t : 0;
+      e += __shfl_xor(e, off, 64);
+    }
+    if (lane == 63) {
+      sm_wsum[wave] = v;
+      sm_went[wave] = e;
+    }
+    __syncthreads();
+    int before = carry;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int t = sm_wsum[w];
+      before += w < wave ? t : 0;
+      carry += t;
+      entries += sm_went[w];
+    }
+    if (s < S) sm_pre[s + 1] = before + v;
+    __syncthreads();
+  }
+  auto pre_at = [&](int i) { return __builtin_amdgcn_readfirstlane(sm_pre[i]); };
+  const int total = pre_at(S);
+  // With one row tile per (sequence, KV head) and no more table entries than
+  // pool blocks, no K/V line is read twice (a block shared by sequences
+  // needs more entries than blocks): the loads then carry the non-temporal
+  // hint, which streams them past the caches.  Otherwise the lines are kept.
+  const bool stream = Rmax == 1 && __builtin_amdgcn_readfirstlane(entries) <= a.pool_blocks;
+  const int nwaves = gridDim.x * kWaves;
+  const int chunk = max(1, (total + nwaves - 1) / nwaves);
+  if (blockIdx.x == 0) {
+    if (tid == 0) {
+      a.plan[0] = chunk;
+      a.plan[1] = total;
+    }
+    for (int s = tid; s <= S; s += kThreads) a.plan[2 + s] = sm_pre[s];
+  }
+  const int wid = blockIdx.x * kWaves + wave;
+  int f = wid * chunk;
+  const int f_end = min(f + chunk, total);
+  // the first item's sequence: pre[s] <= f < pre[s + 1] (found while the
+  // prefix sums are still in LDS)
+  int s = 0, r0 = 0;
+  if (f < total) {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre_at(mid) <= f) lo = mid;
+      else hi = mid - 1;
+    }
+    s = lo;
+    r0 = f - pre_at(s);
+  }
+  __syncthreads();   // from here the LDS holds V stages
+  if (f >= total) return;
+
+  char* st0 = sm_stage + wave * Wk::kStageBytes;   // K stage
+  char* st1 = sm_stage + (kWaves + wave) * Wk::kStageBytes;   // V stage
+  if (stream)
+    mq_split_wave<DT, B, true>(a, s, r0, f, f_end, wid, st0, st1);
+  else
+    mq_split_wave<DT, B, false>(a, s, r0, f, f_end, wid, st0, st1);
+}
+
+// Merge of the split kernel's pieces: thread c owns 4 consecutive dims of one
+// (query token, head) of sequence blockIdx.y.  Its row r = i G + h of KV head
+// g is row r % 32 of row tile rt = r / 32; that unit's items are
+// [a0, a0 + c) with a0 = pre[s] + (g R + rt) c, its tiles the last
+// c - kMqSegItems, so the waves (a0 + kMqSegItems) / chunk ..
+// (a0 + c - 1) / chunk covered it, wave w leaving its piece in slot
+// (s Hk + g) Rmax + rt + w.  Sequences without keys get zero rows.
+template <int D>
+__global__ __launch_bounds__(256) void mq_split_merge_kernel(const AttnArgs a) {
+  constexpr int kChunks = D / 4;
+  const int H = a.num_heads, Hk = a.num_kv_heads, G = a.group;
+  const int Rmax = (a.max_q_len * G + 31) / 32;
+  const int s = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int per_tok = H * kChunks;
+  const int qi = idx / per_tok;
+  const int hq = (idx % per_tok) / kChunks, d0 = (idx % kChunks) * 4;
+  const ConstI32Ptr lens = as_const(a.context_lens), qoff = as_const(a.q_offsets);
+  const MqSeqShape sh = mq_seq_shape(a, lens, qoff, s);
+  if (qi >= sh.n) return;
+  const size_t orow = (size_t)(qoff[s] + qi) * H + hq;
+  if (sh.L == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out(a.out, orow * D + d0 + e, 0.f, a.out_dtype);
+    if (a.lse && d0 == 0) a.lse[orow] = kNegInf;
+    return;
+  }
+  const int g = hq / G, h = hq - g * G;
+  const int r = qi * G + h, rt = r / 32, row = r % 32;
+  const ConstI32Ptr plan = as_const(a.plan);
+  const int chunk = plan[0];
+  const int c = sh.nt + kMqSegItems;
+  const int a0 = plan[2 + s] + (g * sh.R + rt) * c;
+  const int w0 = (a0 + kMqSegItems) / chunk, w1 = (a0 + c - 1) / chunk;
+  if (w0 == w1) return;                // written by its one wave
+  const size_t base = (size_t)(s * Hk + g) * Rmax + rt;
+  constexpr int kBatch = 8;
+  float M = kNegInf, den = 0.f;
+  float num[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int w = w0; w <= w1; w += kBatch) {
+    float pm[kBatch], pl[kBatch];
+    float4 pv[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const size_t sl = (base + min(w + q, w1)) * 32 + row;   // past the last piece: weight 0
+      pm[q] = a.ws_ml[2 * sl];
+      pl[q] = a.ws_ml[2 * sl + 1];
+      pv[q] = *reinterpret_cast<const float4*>(a.ws_o + sl * D + d0);
+    }
+    float mx = M;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      if (w + q <= w1) mx = fmaxf(mx, pm[q]);
+    const float ms = (mx == kNegInf) ? 0.f : mx;
+    const float rs = fast_exp2(M - ms);
+    den *= rs;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[e] *= rs;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const float wt = (w + q <= w1) ? fast_exp2(pm[q] - ms) : 0.f;
+      num[0] = __builtin_fmaf(wt, pv[q].x, num[0]);
+      num[1] = __builtin_fmaf(wt, pv[q].y, num[1]);
+      num[2] = __builtin_fmaf(wt, pv[q].z, num[2]);
+      num[3] = __builtin_fmaf(wt, pv[q].w, num[3]);
+      den = __builtin_fmaf(wt, pl[q], den);
+    }
+    M = mx;
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) store_out(a.out, orow * D + d0 + e, num[e] * inv, a.out_dtype);
+  if (a.lse && d0 == 0) a.lse[orow] = lse2_of(M, den);
+}
+
 hipError_t launch_merge(int head_dim, int num_seqs, const AttnArgs& a, hipStream_t st);
 
 template <int DT, int D, int B>
 static hipError_t launch_mfma_t(int num_seqs, const AttnArgs& a, hipStream_t st,
                                 const KernelEvents& ev) {
+  if constexpr (D == 128) {
+    if (a.plan) {   // balanced split (the host chose it for this shape)
+      hipError_t e = launch_main(multiq_split_kernel<DT, B>, dim3(a.split_workgroups),
+                                 dim3(kThreads), 0, st, ev, a);
+      if (e != hipSuccess) return e;
+      const int per_seq = a.max_q_len * a.num_heads * (D / 4);
+      hipLaunchKernelGGL((mq_split_merge_kernel<D>), dim3((per_seq + 255) / 256, num_seqs),
+                         dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  if (a.plan) return hipErrorNotSupported;
   const int rt_count = (a.max_q_len * a.group + 31) / 32;
   const bool rows = multiq_rows_mode(a.max_q_len, a.group);
   const int units = rows ? (rt_count + kWaves - 1) / kWaves : rt_count;
@@ -603,6 +1117,31 @@ static hipError_t dispatch_mfma(int head_dim, int block_size, int num_seqs, cons
                                 hipStream_t st, const KernelEvents& ev) {
   if (head_dim == 64) return dispatch_mfma_b<DT, 64>(block_size, num_seqs, a, st, ev);
   return dispatch_mfma_b<DT, 128>(block_size, num_seqs, a, st, ev);
+}
+
+// Resident workgroups per CU of the split kernel (occupancy query, cached;
+// threads that race on the first query store the same value, atomically).
+template <int DT, int B>
+static int mq_split_wgs_per_cu() {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (!n) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(multiq_split_kernel<DT, B>), kThreads, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    cached.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+int multiq_split_workgroups_per_cu(int dtype, int block_size) {
+  const bool f16 = dtype == PA_F16;
+  switch (block_size) {
+    case 8: return f16 ? mq_split_wgs_per_cu<PA_F16, 8>() : mq_split_wgs_per_cu<PA_BF16, 8>();
+    case 16: return f16 ? mq_split_wgs_per_cu<PA_F16, 16>() : mq_split_wgs_per_cu<PA_BF16, 16>();
+    default: return f16 ? mq_split_wgs_per_cu<PA_F16, 32>() : mq_split_wgs_per_cu<PA_BF16, 32>();
+  }
 }
 
 hipError_t launch_multiq(int dtype, int head_dim, int block_size, int group, int num_seqs,

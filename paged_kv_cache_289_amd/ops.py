@@ -40,6 +40,7 @@ SIGNATURES = {
     "paged_kv_gather": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "paged_attn_check_inputs": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "paged_attn_default_partition": (_I, [_I, _I, _I, _I, _I, _I]),
+    "paged_attn_multiq_uses_split": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "paged_attn_set_kernel_events": (_I, [_P, _P]),
     "paged_attn_status_string": (ctypes.c_char_p, [_I]),
     "paged_attn_shared_prefix_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
@@ -135,6 +136,15 @@ def default_partition(num_seqs, num_heads, num_kv_heads, block_size, max_context
                       max_q_len=1) -> int:
     return LIB.paged_attn_default_partition(num_seqs, num_heads, num_kv_heads, block_size,
                                             max_context_len, max_q_len)
+
+
+def multiq_uses_split(num_seqs, max_q_len, num_heads, num_kv_heads, head_dim, dtype,
+                      partition_tokens=0) -> bool:
+    """Whether :func:`multiq` with these sizes takes the balanced split (else fixed
+    partitions); ``dtype`` is a torch dtype or a pa_dtype code."""
+    code = dtype if isinstance(dtype, int) else _TORCH_DT[dtype]
+    return bool(LIB.paged_attn_multiq_uses_split(num_seqs, max_q_len, num_heads, num_kv_heads,
+                                                 head_dim, code, partition_tokens))
 
 
 def workspace_size(num_seqs, total_q, max_q_len, num_heads, num_kv_heads, head_dim, block_size,

@@ -12,6 +12,7 @@ hipError_t launch_decode(int, int, int, int, int, const AttnArgs&, hipStream_t,
   return hipErrorNoDevice;
 }
 int split_workgroups_per_cu(int, int, int, int) { return 1; }
+int multiq_split_workgroups_per_cu(int, int) { return 1; }
 hipError_t launch_multiq(int, int, int, int, int, const AttnArgs&, hipStream_t,
                          const KernelEvents&) {
   return hipErrorNoDevice;

@@ -167,11 +167,41 @@ def test_workspace_size_formula():
     slots = 64 * 8 + 8192
     assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 0) == \
         512 + slots * 4 * 2 * 4 + slots * 4 * 128 * 4
-    # multi-token rows whose contexts fit one partition need no workspace
-    assert ops.workspace_size(2, 10, 5, 32, 8, 128, 16, 256, 0) == 0
+    # multi-token rows whose contexts fit one partition need no workspace with an
+    # explicit partition size
+    assert ops.workspace_size(2, 10, 5, 32, 8, 128, 16, 256, 256) == 0
+    # ... while the library's own split (5 tokens x G 4 = 20 rows: one row tile per
+    # KV head) holds a 32-row piece per (sequence, KV head, row tile) unit and per
+    # wave: 2*8 = 16 units of 256/32 + 2 items each = 160 waves at most; the plan
+    # (2 + 3 int32, on 256 bytes), then fp32 (max, sum) and 128 outputs per row
+    rows = (16 + 160) * 32
+    assert ops.workspace_size(2, 10, 5, 32, 8, 128, 16, 256, 0) == \
+        256 + rows * 2 * 4 + rows * 128 * 4
+    # the waves stop at 4096 (64 sequences of up to 8192 keys)
+    rows = (64 * 8 + 4096) * 32
+    assert ops.workspace_size(64, 320, 5, 32, 8, 128, 16, 8192, 0) == \
+        512 + rows * 2 * 4 + rows * 128 * 4
     assert ops.workspace_size(64, 64, 1, 32, 8, 128, 16, 4096, 24) == 0     # rejected
     assert ops.default_partition(64, 32, 8, 16, 4096, 1) % 16 == 0
     assert ops.default_partition(1, 32, 8, 16, 4608, 512) % 32 == 0
+
+
+def test_multiq_split_choice():
+    """Which multi-token calls take the balanced split: bf16/f16, head_dim 128, the
+    library's own work split, 2 or more query tokens and at most three 32-row tiles
+    of rows per KV head."""
+    bf, f16, f32 = ops.PA_BF16, ops.PA_F16, ops.PA_F32
+    assert ops.multiq_uses_split(64, 5, 32, 8, 128, bf)            # 20 rows per KV head
+    assert ops.multiq_uses_split(64, 5, 32, 8, 128, f16)
+    assert ops.multiq_uses_split(4, 24, 32, 8, 128, bf)            # 96 rows: three tiles
+    assert not ops.multiq_uses_split(4, 25, 32, 8, 128, bf)        # 100 rows: row groups
+    assert not ops.multiq_uses_split(64, 5, 32, 8, 128, f32)       # vector-ALU path
+    assert not ops.multiq_uses_split(64, 5, 32, 8, 64, bf)         # head_dim 64
+    assert not ops.multiq_uses_split(64, 5, 32, 8, 128, bf, 256)   # explicit partitions
+    assert not ops.multiq_uses_split(64, 1, 32, 8, 128, bf)        # one token per sequence
+    assert not ops.multiq_uses_split(8193, 2, 32, 8, 128, bf)      # past 8192 sequences
+    assert not ops.multiq_uses_split(2048, 5, 32, 16, 128, bf)     # past 16384 units
+    assert ops.multiq_uses_split(2048, 5, 32, 8, 128, bf)          # 16384 units
 
 
 def _shared(**kw):
