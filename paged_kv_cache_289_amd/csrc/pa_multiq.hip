@@ -34,6 +34,7 @@
 // (rows layout): four row tiles per workgroup share each staged K/V tile.
 // fp32: every query row runs the decode kernel over its own visible length.
 #include <atomic>
+#include <type_traits>
 
 #include "pa_common.h"
 
@@ -275,9 +276,15 @@ struct TokenTileWalker {
   // NT: the non-temporal hint.
   template <bool NT>
   __device__ __forceinline__ void load_k(int t0, char* stage) const {
+    load_k_part<NT, 8>(t0, stage, 0);
+  }
+  // instructions i0 .. i0 + N - 1 of load_k (tile rows 4 i0 .. 4 (i0 + N) - 1)
+  template <bool NT, int N>
+  __device__ __forceinline__ void load_k_part(int t0, char* stage, int i0) const {
     const int krow = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int j = 0; j < N; ++j) {
+      const int i = i0 + j;
       const int r = 4 * i + krow;
       const int t = min(t0 + r, L - 1);
       const char* src = kbase + row_off(phys_of(t0, t), t) + (((lane & 15) ^ (r & 15)) * 16);
@@ -301,14 +308,96 @@ struct TokenTileWalker {
   // which holds chunk (l % 16) ^ 4 (l / 16)
   template <bool NT>
   __device__ __forceinline__ void load_v(int t0, char* stage) const {
+    load_v_part<NT, 8>(t0, stage, 0);
+  }
+  template <bool NT, int N>
+  __device__ __forceinline__ void load_v_part(int t0, char* stage, int i0) const {
     const int vrow = lane >> 4, vchunk = (lane & 15) ^ (4 * (lane >> 4));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int j = 0; j < N; ++j) {
+      const int i = i0 + j;
       const int t = min(t0 + 4 * i + vrow, L - 1);
       const char* src = vbase + row_off(phys_of(t0, t), t) + vchunk * 16;
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(stage + 1024 * i),
                                        16, 0, NT ? kCpolNt : 0);
     }
+  }
+
+  // This lane's byte offsets, inside a stage, of its K operand chunks
+  // (k-steps 0..7, as read_k) and of its V^T rows (dim blocks 0..3, as
+  // read_vt; the second 16-token step and the second half of each add 4096
+  // and 2048), plus `base`.
+  __device__ __forceinline__ void lane_offsets(unsigned base, unsigned (&koff)[KS],
+                                               unsigned (&voff)[DB]) const {
+    const int m = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      koff[ks] = base + m * kRowBytes + (((2 * ks + hh) ^ (m & 15)) * 16);
+    const int rsub = (lane & 15) / 4;
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      voff[db] = base + (4 * hh + rsub) * kRowBytes + (((4 * db + cl) ^ (4 * rsub)) * 16) +
+                 (lane & 1) * 8;
+  }
+  // read_k and read_vt of one stage (K at byte KO past the offsets' base, V at
+  // KO + 8192) in one asm block that ends by waiting for its own reads.  For
+  // a stage read while loads into other stages are in flight: the compiler,
+  // which cannot tell the stages apart, would wait for every load in flight
+  // before a read it issues itself.
+  template <int KO>
+  __device__ __forceinline__ void read_stage_asm(const unsigned (&koff)[KS],
+                                                 const unsigned (&voff)[DB], uint4 (&kr)[KS],
+                                                 uint4 (&va)[DB][2]) const {
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+    u4v k[8];
+    u2v v[4][4];
+    asm volatile(
+        "ds_read_b128 %0, %24 offset:%36\n\t"
+        "ds_read_b128 %1, %25 offset:%36\n\t"
+        "ds_read_b128 %2, %26 offset:%36\n\t"
+        "ds_read_b128 %3, %27 offset:%36\n\t"
+        "ds_read_b128 %4, %28 offset:%36\n\t"
+        "ds_read_b128 %5, %29 offset:%36\n\t"
+        "ds_read_b128 %6, %30 offset:%36\n\t"
+        "ds_read_b128 %7, %31 offset:%36\n\t"
+        "ds_read_b64_tr_b16 %8, %32 offset:%37\n\t"
+        "ds_read_b64_tr_b16 %9, %32 offset:%38\n\t"
+        "ds_read_b64_tr_b16 %10, %32 offset:%39\n\t"
+        "ds_read_b64_tr_b16 %11, %32 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %12, %33 offset:%37\n\t"
+        "ds_read_b64_tr_b16 %13, %33 offset:%38\n\t"
+        "ds_read_b64_tr_b16 %14, %33 offset:%39\n\t"
+        "ds_read_b64_tr_b16 %15, %33 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %16, %34 offset:%37\n\t"
+        "ds_read_b64_tr_b16 %17, %34 offset:%38\n\t"
+        "ds_read_b64_tr_b16 %18, %34 offset:%39\n\t"
+        "ds_read_b64_tr_b16 %19, %34 offset:%40\n\t"
+        "ds_read_b64_tr_b16 %20, %35 offset:%37\n\t"
+        "ds_read_b64_tr_b16 %21, %35 offset:%38\n\t"
+        "ds_read_b64_tr_b16 %22, %35 offset:%39\n\t"
+        "ds_read_b64_tr_b16 %23, %35 offset:%40\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(k[0]), "=v"(k[1]), "=v"(k[2]), "=v"(k[3]), "=v"(k[4]), "=v"(k[5]), "=v"(k[6]),
+          "=v"(k[7]), "=v"(v[0][0]), "=v"(v[0][1]), "=v"(v[0][2]), "=v"(v[0][3]),
+          "=v"(v[1][0]), "=v"(v[1][1]), "=v"(v[1][2]), "=v"(v[1][3]), "=v"(v[2][0]),
+          "=v"(v[2][1]), "=v"(v[2][2]), "=v"(v[2][3]), "=v"(v[3][0]), "=v"(v[3][1]),
+          "=v"(v[3][2]), "=v"(v[3][3])
+        : "v"(koff[0]), "v"(koff[1]), "v"(koff[2]), "v"(koff[3]), "v"(koff[4]), "v"(koff[5]),
+          "v"(koff[6]), "v"(koff[7]), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
+          "i"(KO), "i"(KO + 8192), "i"(KO + 8192 + 2048), "i"(KO + 8192 + 4096),
+          "i"(KO + 8192 + 6144)
+        : "memory");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kr[ks] = make_uint4(k[ks].x, k[ks].y, k[ks].z, k[ks].w);
+    // per dim block: 16-token step 0 (rows, rows + 8), then step 1
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        va[db][ks] = make_uint4(v[db][2 * ks].x, v[db][2 * ks].y, v[db][2 * ks + 1].x,
+                                v[db][2 * ks + 1].y);
   }
 
   // The tiles t0, t0 + stride, ... below t_end (t0 < t_end, wave-uniform)
@@ -522,9 +611,15 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
   constexpr int kVTile = 32 * kRowBytes;
   __shared__ __attribute__((aligned(16))) char sm_kst[kStaged ? kWaves * kVTile : 16];
   __shared__ __attribute__((aligned(16))) char sm_vst[kStaged ? kWaves * kVTile : 16];
-  // rows layout: 32-token tiles per loop step, and two LDS stages of a step each
+  // rows layout at head_dim 128: four stages, each a K tile and then its V
+  // tile (16 KiB), filled by direct-to-LDS loads
+  constexpr bool kPipe = ROWS && D == 128;
+  constexpr int kPipeStage = 2 * 32 * kRowBytes;
+  __shared__ __attribute__((aligned(16))) char sm_pipe[kPipe ? 4 * kPipeStage : 16];
+  // rows layout at head_dim 64: 32-token tiles per loop step, and two LDS
+  // stages of a step each
   constexpr int kTps = 1;
-  constexpr int kLdsBytes = ROWS ? 2 * kTps * kStageBytes : 16;   // (only the rows layout stages)
+  constexpr int kLdsBytes = (ROWS && !kPipe) ? 2 * kTps * kStageBytes : 16;
   __shared__ __attribute__((aligned(16))) char sm_kv[kLdsBytes];
   // base: K tile, base + kTileBytes: V tile
   auto stage_store = [&](char* base, const u32x4_t (&sk)[kPer], const u32x4_t (&sv)[kPer]) {
@@ -587,7 +682,97 @@ __device__ __forceinline__ void multiq_mfma_body(const AttnArgs& a) {
     }
   };
 
-  if constexpr (ROWS) {
+  if constexpr (kPipe) {
+    // All four waves walk the workgroup's tiles tok0 + 32 i, i < nT, in step.
+    // Tile i sits in stage i mod 4; each wave loads a quarter of it (two of
+    // the eight load instructions of K and two of V, tile rows 8 wave ..
+    // 8 wave + 7) three steps ahead.  Step i: wait for this wave's loads of
+    // tile i (the eight issued after them, tiles i + 1 and i + 2, stay in
+    // flight), a barrier (every wave's quarter has landed, and every wave is
+    // past step i - 1, whose stage the loads of tile i + 3 then overwrite),
+    // read this wave's operands, issue tile i + 3, compute.  Past the last
+    // tile the loads repeat tile nT - 1 into a stage nobody reads again, so
+    // every step issues the same loads and waits the same count.  The loop
+    // bounds are workgroup-uniform, so every wave reaches every barrier; a
+    // wave whose rows see no key of a tile skips its reads and compute.
+    const TokenTileWalker<B> w{kbase, vbase, tblc, jlast, L, Hk, g, lane};
+    const unsigned pipe0 = (unsigned)(size_t)(__attribute__((address_space(3))) char*)sm_pipe;
+    unsigned koff[KS], voff[DB];
+    w.lane_offsets(pipe0, koff, voff);
+    // full tiles: this lane's byte offsets inside the block of its rows, for
+    // load instruction j of this wave (row r = 8 wave + 4 j + lane / 16 of
+    // the tile, at slot r mod B of block r / B; position lane % 16 holds
+    // chunk (lane % 16) ^ (r mod 16) of K, (lane % 16) ^ 4 (r mod 4) of V)
+    const int lrow = lane >> 4;
+    const unsigned lck = (unsigned)((lane & 15) ^ lrow);
+    const unsigned cv = (unsigned)(((lane & 15) ^ (4 * lrow)) << 4);
+    const size_t head_off = (size_t)g * B * kRowBytes;
+    const int nT = (wg_end - tok0 + 31) / 32;   // >= 1
+    auto issue = [&](int i, char* st) {
+      const int t0 = tok0 + 32 * min(i, nT - 1);
+      if (t0 + 32 <= L) {   // workgroup-uniform: block ids and bases are scalar
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = 8 * wave + 4 * j;   // the instruction's first row
+          const size_t boff = ((size_t)tblc[(t0 + r) / B] * Hk) * B * kRowBytes + head_off;
+          const unsigned row = (unsigned)((r % B + lrow) * kRowBytes);
+          const unsigned offk = row + ((lck ^ (unsigned)(r & 12)) << 4);
+          char* dst = st + 1024 * (2 * wave + j);
+          __builtin_amdgcn_global_load_lds(kbase + boff + offk,
+                                           (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vbase + boff + row + cv,
+                                           (__attribute__((address_space(3))) void*)(dst + 8192),
+                                           16, 0, 0);
+        }
+      } else {
+        w.template load_k_part<false, 2>(t0, st, 2 * wave);
+        w.template load_v_part<false, 2>(t0, st + 8192, 2 * wave);
+      }
+    };
+    // the query operands first (vmcnt(0)): with them still in flight at the
+    // loop the compiler would wait for every load before entering it
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    issue(0, sm_pipe);
+    issue(1, sm_pipe + kPipeStage);
+    issue(2, sm_pipe + 2 * kPipeStage);
+    auto step = [&](int i, auto stage) {
+      constexpr int S = decltype(stage)::value;
+      // s_waitcnt vmcnt(8), other counters untouched; then a bare barrier
+      // (__syncthreads() also fences global memory, which would wait for
+      // every load in flight)
+      __builtin_amdgcn_s_waitcnt(0x0F78);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const int t0 = tok0 + 32 * i;
+      const bool mine = t0 < tok_end;   // wave-uniform
+      uint4 kr[KS], va[DB][2];
+      if (mine) w.template read_stage_asm<S * kPipeStage>(koff, voff, kr, va);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(i + 3, sm_pipe + ((S + 3) % 4) * kPipeStage);
+      __builtin_amdgcn_sched_barrier(0);
+      if (mine) {
+        uint4 pb0, pb1, pl0, pl1;
+        softmax_scores(t0, qk_tile(kr), pb0, pb1, pl0, pl1);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) pv_block(db, va[db][0], va[db][1], pb0, pb1, pl0, pl1);
+      }
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    for (int i = 0; i < nT; i += 4) {
+      step(i, S0{});
+      if (i + 1 >= nT) break;
+      step(i + 1, S1{});
+      if (i + 2 >= nT) break;
+      step(i + 2, S2{});
+      if (i + 3 >= nT) break;
+      step(i + 3, S3{});
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no load into LDS outlives the wave
+  } else if constexpr (ROWS) {
     // All four waves walk the workgroup's tokens [tok0, wg_end) in step, kTps
     // 32-token tiles per step: the step's tiles are read from one LDS stage
     // while the next step's are loaded into registers and then stored to the
