@@ -389,6 +389,24 @@ int decode_core(void* out, const void* q, const void* k_cache, const void* v_cac
     a.max_parts = max_parts;
     a.plan = nullptr;
   }
+  if (dtype == PA_FP8_E4M3 && head_dim == 128 && a.plan && !device_sized && len_offset == 0 &&
+      !split_no_merge && partition_tokens == 0 &&
+      (int64_t)num_seqs * num_kv_heads <= pa::kMqMaxSplitUnits && !used) {
+    // The 8-bit cache at head_dim 128: the same balanced split, over
+    // (sequence, KV head, 32-token tile) items, with the products on the
+    // matrix cores (the multi-query split kernel without query offsets).  Its
+    // pieces use the decode's slots (S Hk + waves) x G, within the workspace
+    // checked above (at most kMqMaxSplitWaves waves).
+    const int wgs = pa::multiq_split_workgroups_per_cu(PA_FP8_E4M3, block_size);
+    const int waves = mq_split_waves((int64_t)num_seqs * num_kv_heads, max_context_len,
+                                     device_cus() * wgs * pa::kWaves);
+    split_workspace_ptrs(workspace, num_seqs, num_heads, num_kv_heads, head_dim, waves, &a);
+    a.split_workgroups = waves / pa::kWaves;
+    a.chunk_blocks = 0;
+    hipError_t e = pa::launch_fp8_split_decode(block_size, num_seqs, a,
+                                               static_cast<hipStream_t>(stream), ev);
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+  }
   if (used) *used = a;
   hipError_t e = pa::launch_decode(dtype, head_dim, block_size, a.group, num_seqs, a,
                                    static_cast<hipStream_t>(stream), ev);

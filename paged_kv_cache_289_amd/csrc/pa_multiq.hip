@@ -962,6 +962,153 @@ __global__ __launch_bounds__(kThreads, 2) void multiq_mfma_rows_kernel(const Att
   multiq_mfma_body<DT, D, B, true>(a);
 }
 
+// 8-bit E4M3 K/V at head_dim 128 (the decode of an 8-bit cache through the
+// balanced split): the codes of a 32-token tile reach the wave's stages by
+// direct-to-LDS loads (a wave instruction moves eight 128-byte rows) and are
+// widened to f16 on their way into the operands (exact: every E4M3 value is an
+// f16 value); the products run in f16 with fp32 accumulation.  Stages: the K
+// codes (4 KiB) and the V codes (4 KiB) in one 8 KiB stage, and V widened to
+// f16 in a second 8 KiB stage with the 16-bit layout, read by transpose reads.
+template <int B>
+struct Fp8TileWalker {
+  static constexpr int kRowBytes = 128;   // 128 codes
+  static constexpr int kTileBlocks = 32 / B;
+  static constexpr int KS = 8, DB = 4;
+  const char* kbase;
+  const char* vbase;
+  ConstI32Ptr tblc;   // the sequence's block table
+  int jlast;          // its last block, (L - 1) / B
+  int L, Hk, g, lane;
+
+  __device__ __forceinline__ int phys_of(int t0, int t) const {
+    const int jt = t / B - t0 / B;
+    int phys = tblc[min(t0 / B, jlast)];
+#pragma unroll
+    for (int k = 1; k < kTileBlocks; ++k) {
+      const int id = tblc[min(t0 / B + k, jlast)];
+      phys = (jt == k) ? id : phys;
+    }
+    return phys;
+  }
+  __device__ __forceinline__ size_t row_off(int phys, int t) const {
+    return (((size_t)phys * Hk + g) * B + (t % B)) * kRowBytes;
+  }
+  // instruction i: lane l writes stage bytes 1024 i + 16 l, i.e. row
+  // r = 8 i + l / 8 at position l % 8, which holds 16-byte chunk
+  // (l % 8) ^ ((r / 2) mod 8) of K, (l % 8) ^ ((r / 2) mod 4) of V
+  template <bool NT, int MASK>
+  __device__ __forceinline__ void load_codes(const char* base, int t0, char* stage) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const int t = min(t0 + r, L - 1);   // >= t0, since t0 < L
+      const char* src = base + row_off(phys_of(t0, t), t) + (((lane & 7) ^ ((r >> 1) & MASK)) * 16);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(stage + 1024 * i),
+                                       16, 0, NT ? kCpolNt : 0);
+    }
+  }
+  // eight codes (two words) -> eight f16 (one 16-byte operand)
+  __device__ static __forceinline__ uint4 widen8(uint32_t w0, uint32_t w1) {
+    const auto a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    const auto b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    const auto c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    const auto d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                      __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+  }
+  // K operands: lane (m, hh), k-step ks: codes 16 ks + 8 hh .. + 7 of row m
+  // (chunk ks at position ks ^ ((m / 2) mod 8): the 16 rows of one lane half
+  // fall on distinct banks)
+  __device__ __forceinline__ void read_k(const char* stage, uint4 (&kr)[KS]) const {
+    typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+    const int m = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int pos = ks ^ ((m >> 1) & 7);
+      const u2v x = *(__attribute__((address_space(3))) const u2v*)(
+          __attribute__((address_space(3))) const char*)(stage + m * kRowBytes + pos * 16 + hh * 8);
+      kr[ks] = widen8(x.x, x.y);
+    }
+  }
+  // V codes -> f16 rows of 256 bytes, 16-byte chunk c of row r at position
+  // c ^ 4 (r mod 4): lane l widens half l % 2 of row l / 2
+  __device__ __forceinline__ void widen_v(const char* v8, char* v16) const {
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    const int r = lane >> 1, h = lane & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 4 * h + j;            // codes 16 c .. 16 c + 15
+      const u4v x = *(__attribute__((address_space(3))) const u4v*)(
+          __attribute__((address_space(3))) const char*)(v8 + r * kRowBytes + ((c ^ ((r >> 1) & 3)) * 16));
+      const uint4 lo = widen8(x.x, x.y), hi = widen8(x.z, x.w);
+      *(__attribute__((address_space(3))) u4v*)(__attribute__((address_space(3))) char*)(
+          v16 + r * 256 + (((2 * c) ^ (4 * (r & 3))) * 16)) = u4v{lo.x, lo.y, lo.z, lo.w};
+      *(__attribute__((address_space(3))) u4v*)(__attribute__((address_space(3))) char*)(
+          v16 + r * 256 + (((2 * c + 1) ^ (4 * (r & 3))) * 16)) = u4v{hi.x, hi.y, hi.z, hi.w};
+    }
+  }
+  // The tiles t0, t0 + stride, ... below t_end, as TokenTileWalker::walk:
+  // each step reads its K operands and widens its V, then (once those LDS
+  // accesses are back) loads the next tile's codes into the same stage.
+  // kst: the K codes, then the V codes; v16: V in f16.
+  template <bool NT>
+  __device__ __forceinline__ void walk(int t0, int t_end, int stride, const uint4 (&qv)[KS],
+                                       float c, int lim, int unmask_end, char* kst, char* v16,
+                                       f32x16_t (&o)[DB], float& m_run, float& l_run) const {
+    const int hh = lane >> 5;
+    const TokenTileWalker<B> t16{nullptr, nullptr, tblc, jlast, L, Hk, g, lane};
+    t_end = __builtin_amdgcn_readfirstlane(t_end);
+    load_codes<NT, 7>(kbase, t0, kst);
+    load_codes<NT, 3>(vbase, t0, kst + 4096);
+    for (;;) {
+      uint4 kr[KS];
+      read_k(kst, kr);
+      widen_v(kst + 4096, v16);
+      uint4 va[DB][2];
+      t16.read_vt(v16, va);
+      const bool more = t0 + stride < t_end;   // wave-uniform
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the stage is read
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        load_codes<NT, 7>(kbase, t0 + stride, kst);
+        load_codes<NT, 3>(vbase, t0 + stride, kst + 4096);
+      }
+      const f32x16_t sc = tile_qk<PA_F16>(kr, qv);
+      uint4 pb0, pb1, pl0, pl1;
+      tile_softmax<PA_F16>(sc, t0, hh, t0 + 32 <= unmask_end, lim, c, m_run, l_run, o, pb0, pb1,
+                           pl0, pl1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        tile_pv<PA_F16>(o[db], va[db][0], va[db][1], pb0, pb1, pl0, pl1);
+      if (!more) break;
+      t0 += stride;
+    }
+  }
+};
+
+// Q^T operand in f16 from bf16 queries (the 8-bit cache's queries): exact for
+// |q| in f16's normal range; a negative scale flips the f16 sign bits.
+__device__ __forceinline__ void load_q_operand_f16(const void* q, size_t out_row, int hh,
+                                                   bool row_ok, float scale_log2,
+                                                   uint4 (&qv)[8]) {
+  constexpr int D = 128;
+  const uint4* qp = reinterpret_cast<const uint4*>(q) + (out_row * D + hh * 8) / 8;
+  auto cv = [](uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
+                                                                   __uint_as_float(w & 0xffff0000u)));
+  };
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const uint4 x = row_ok ? qp[2 * ks] : make_uint4(0, 0, 0, 0);
+    qv[ks] = make_uint4(cv(x.x), cv(x.y), cv(x.z), cv(x.w));
+    if (scale_log2 < 0.f) {
+      qv[ks].x ^= 0x80008000u; qv[ks].y ^= 0x80008000u;
+      qv[ks].z ^= 0x80008000u; qv[ks].w ^= 0x80008000u;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // balanced split (token layout, head_dim 128)
 // ---------------------------------------------------------------------------
@@ -986,7 +1133,8 @@ __device__ __forceinline__ MqSeqShape mq_seq_shape(const AttnArgs& a, ConstI32Pt
                                                    ConstI32Ptr qoff, int s) {
   MqSeqShape r;
   r.L = min(max(lens[s], 0), a.max_context_len);
-  r.n = min(max(qoff[s + 1] - qoff[s], 0), a.max_q_len);
+  // (no query offsets: a decode, one query token per sequence)
+  r.n = a.q_offsets ? min(max(qoff[s + 1] - qoff[s], 0), a.max_q_len) : 1;
   r.R = (r.n * a.group + 31) / 32;
   r.nt = (r.L + 31) / 32;
   if (r.R == 0 || r.nt == 0) r.R = r.nt = 0;
@@ -1002,6 +1150,8 @@ __device__ __forceinline__ void mq_split_wave(const AttnArgs& a, int s, int r0, 
   constexpr int D = 128, KS = Wk::KS, DB = Wk::DB, X = kMqSegItems;
   const int H = a.num_heads, Hk = a.num_kv_heads, G = a.group;
   const int Rmax = (a.max_q_len * G + 31) / 32;
+  // rows per piece slot: a row tile, or for a decode the group's G rows
+  const int prow = a.q_offsets ? 32 : G;
   const int lane = threadIdx.x & 63;
   const ConstI32Ptr lens = as_const(a.context_lens), qoff = as_const(a.q_offsets);
   MqSeqShape sh = mq_seq_shape(a, lens, qoff, s);
@@ -1031,23 +1181,32 @@ __device__ __forceinline__ void mq_split_wave(const AttnArgs& a, int s, int r0, 
     const int lrow = row_ok ? visible(qi) : 0;
     const int l_tile_max = visible(min(rt * 32 + 31, n_rows - 1) / G);
     const int l_tile_min = visible((rt * 32) / G);
-    const size_t out_row = (size_t)(qoff[s] + qi) * H + (size_t)g * G + qh;
+    const size_t out_row = (size_t)((a.q_offsets ? qoff[s] : s) + qi) * H + (size_t)g * G + qh;
     uint4 qv[KS];
-    load_q_operand<D>(a.q, out_row, hh, row_ok, a.scale_log2, qv);
+    if constexpr (DT == PA_FP8_E4M3)
+      load_q_operand_f16(a.q, out_row, hh, row_ok, a.scale_log2, qv);
+    else
+      load_q_operand<D>(a.q, out_row, hh, row_ok, a.scale_log2, qv);
     f32x16_t o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16_t{};
     float m_run = kMaxInit, l_run = 0.f;
     const int seg_end = min(32 * (j + n_here), l_tile_max);
     if (32 * j < seg_end) {            // (a causal row tile may see fewer tiles)
-      const Wk w{kbase, vbase, as_const(a.block_tables + (size_t)s * a.max_blocks_per_seq),
-                 (L - 1) / B, L, Hk, g, lane};
-      w.template walk<DT, NT>(32 * j, seg_end, 32, qv, cs, min(lrow, seg_end),
-                                  min(l_tile_min, seg_end), st0, st1, o, m_run, l_run);
+      const ConstI32Ptr tbl = as_const(a.block_tables + (size_t)s * a.max_blocks_per_seq);
+      if constexpr (DT == PA_FP8_E4M3) {
+        const Fp8TileWalker<B> w{kbase, vbase, tbl, (L - 1) / B, L, Hk, g, lane};
+        w.template walk<NT>(32 * j, seg_end, 32, qv, cs, min(lrow, seg_end),
+                            min(l_tile_min, seg_end), st0, st1, o, m_run, l_run);
+      } else {
+        const Wk w{kbase, vbase, tbl, (L - 1) / B, L, Hk, g, lane};
+        w.template walk<DT, NT>(32 * j, seg_end, 32, qv, cs, min(lrow, seg_end),
+                                min(l_tile_min, seg_end), st0, st1, o, m_run, l_run);
+      }
     }
     if (j == 0 && n_here == sh.nt) {   // the whole unit: final output
       if (row_ok) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        const float inv = l_run > 0.f ? a.out_scale / l_run : 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -1057,7 +1216,7 @@ __device__ __forceinline__ void mq_split_wave(const AttnArgs& a, int s, int r0, 
         if (a.lse && hh == 0) a.lse[out_row] = lse2_of(m_run, l_run);
       }
     } else if (row_ok) {               // a piece: partial for the merge
-      const size_t slot = ((size_t)(s * Hk + g) * Rmax + rt + wid) * 32 + mcol;
+      const size_t slot = ((size_t)(s * Hk + g) * Rmax + rt + wid) * prow + mcol;
       float* po = a.ws_o + slot * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -1086,7 +1245,8 @@ __device__ __forceinline__ void mq_split_wave(const AttnArgs& a, int s, int r0, 
         }
       }
     }
-  }}
+  }
+}
 
 template <int DT, int B>
 __global__ __launch_bounds__(kThreads, 2) void multiq_split_kernel(const AttnArgs a) {
@@ -1204,7 +1364,8 @@ __global__ __launch_bounds__(256) void mq_split_merge_kernel(const AttnArgs a) {
   const ConstI32Ptr lens = as_const(a.context_lens), qoff = as_const(a.q_offsets);
   const MqSeqShape sh = mq_seq_shape(a, lens, qoff, s);
   if (qi >= sh.n) return;
-  const size_t orow = (size_t)(qoff[s] + qi) * H + hq;
+  const size_t orow = (size_t)((a.q_offsets ? qoff[s] : s) + qi) * H + hq;
+  const int prow = a.q_offsets ? 32 : G;   // rows per piece slot
   if (sh.L == 0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) store_out(a.out, orow * D + d0 + e, 0.f, a.out_dtype);
@@ -1228,7 +1389,7 @@ __global__ __launch_bounds__(256) void mq_split_merge_kernel(const AttnArgs a) {
     float4 pv[kBatch];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      const size_t sl = (base + min(w + q, w1)) * 32 + row;   // past the last piece: weight 0
+      const size_t sl = (base + min(w + q, w1)) * prow + row;   // past the last piece: weight 0
       pm[q] = a.ws_ml[2 * sl];
       pl[q] = a.ws_ml[2 * sl + 1];
       pv[q] = *reinterpret_cast<const float4*>(a.ws_o + sl * D + d0);
@@ -1253,7 +1414,7 @@ __global__ __launch_bounds__(256) void mq_split_merge_kernel(const AttnArgs a) {
     }
     M = mx;
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float inv = den > 0.f ? a.out_scale / den : 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) store_out(a.out, orow * D + d0 + e, num[e] * inv, a.out_dtype);
   if (a.lse && d0 == 0) a.lse[orow] = lse2_of(M, den);
@@ -1320,7 +1481,37 @@ static int mq_split_wgs_per_cu() {
   return n;
 }
 
+// The decode of an 8-bit cache at head_dim 128 through the split kernel
+// (AttnArgs without query offsets) and its merge.
+template <int B>
+static hipError_t launch_fp8_split_t(int num_seqs, const AttnArgs& a, hipStream_t st,
+                                     const KernelEvents& ev) {
+  hipError_t e = launch_main(multiq_split_kernel<PA_FP8_E4M3, B>, dim3(a.split_workgroups),
+                             dim3(kThreads), 0, st, ev, a);
+  if (e != hipSuccess) return e;
+  const int per_seq = a.num_heads * (128 / 4);
+  hipLaunchKernelGGL((mq_split_merge_kernel<128>), dim3((per_seq + 255) / 256, num_seqs),
+                     dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_split_decode(int block_size, int num_seqs, const AttnArgs& a,
+                                   hipStream_t st, const KernelEvents& ev) {
+  switch (block_size) {
+    case 8: return launch_fp8_split_t<8>(num_seqs, a, st, ev);
+    case 16: return launch_fp8_split_t<16>(num_seqs, a, st, ev);
+    default: return launch_fp8_split_t<32>(num_seqs, a, st, ev);
+  }
+}
+
 int multiq_split_workgroups_per_cu(int dtype, int block_size) {
+  if (dtype == PA_FP8_E4M3) {
+    switch (block_size) {
+      case 8: return mq_split_wgs_per_cu<PA_FP8_E4M3, 8>();
+      case 16: return mq_split_wgs_per_cu<PA_FP8_E4M3, 16>();
+      default: return mq_split_wgs_per_cu<PA_FP8_E4M3, 32>();
+    }
+  }
   const bool f16 = dtype == PA_F16;
   switch (block_size) {
     case 8: return f16 ? mq_split_wgs_per_cu<PA_F16, 8>() : mq_split_wgs_per_cu<PA_BF16, 8>();
