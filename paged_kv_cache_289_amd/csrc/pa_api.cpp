@@ -389,22 +389,26 @@ int decode_core(void* out, const void* q, const void* k_cache, const void* v_cac
     a.max_parts = max_parts;
     a.plan = nullptr;
   }
-  if (dtype == PA_FP8_E4M3 && head_dim == 128 && a.plan && !device_sized && len_offset == 0 &&
-      !split_no_merge && partition_tokens == 0 &&
-      (int64_t)num_seqs * num_kv_heads <= pa::kMqMaxSplitUnits && !used) {
-    // The 8-bit cache at head_dim 128: the same balanced split, over
-    // (sequence, KV head, 32-token tile) items, with the products on the
-    // matrix cores (the multi-query split kernel without query offsets).  Its
-    // pieces use the decode's slots (S Hk + waves) x G, within the workspace
-    // checked above (at most kMqMaxSplitWaves waves).
-    const int wgs = pa::multiq_split_workgroups_per_cu(PA_FP8_E4M3, block_size);
+  if ((dtype == PA_BF16 || dtype == PA_F16 || dtype == PA_FP8_E4M3) && head_dim == 128 &&
+      a.plan && len_offset == 0 && !split_no_merge && !used && partition_tokens == 0 &&
+      (int64_t)num_seqs * num_kv_heads <= pa::kMqMaxSplitUnits) {
+    // Head_dim 128: the same balanced split, over (sequence, KV head, 32-token
+    // tile) items, with the products on the matrix cores (the multi-query
+    // split kernel without query offsets; an 8-bit cache is widened to f16).
+    // Its pieces use the decode's slots, (S Hk + waves) x G, for at most
+    // kMqMaxSplitWaves waves: within the workspace checked above, and checked
+    // again against the allocation-free entry point's scratch.
+    const int wgs = pa::multiq_split_workgroups_per_cu(dtype, block_size);
     const int waves = mq_split_waves((int64_t)num_seqs * num_kv_heads, max_context_len,
                                      device_cus() * wgs * pa::kWaves);
+    if (device_sized &&
+        workspace_bytes < split_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, waves))
+      return PA_ERR_SCRATCH;
     split_workspace_ptrs(workspace, num_seqs, num_heads, num_kv_heads, head_dim, waves, &a);
     a.split_workgroups = waves / pa::kWaves;
     a.chunk_blocks = 0;
-    hipError_t e = pa::launch_fp8_split_decode(block_size, num_seqs, a,
-                                               static_cast<hipStream_t>(stream), ev);
+    hipError_t e = pa::launch_split_decode(dtype, block_size, num_seqs, a,
+                                           static_cast<hipStream_t>(stream), ev);
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
   if (used) *used = a;

@@ -103,8 +103,10 @@ hipError_t launch_decode(int dtype, int head_dim, int block_size, int group, int
 // Resident workgroups per CU of the split decode kernel for this configuration.
 int split_workgroups_per_cu(int dtype, int head_dim, int block_size, int group);
 int multiq_split_workgroups_per_cu(int dtype, int block_size);
-hipError_t launch_fp8_split_decode(int block_size, int num_seqs, const AttnArgs& a,
-                                   hipStream_t st, const KernelEvents& ev);
+// decode at head_dim 128 (bf16, f16 or 8-bit K/V) through the multi-query
+// balanced-split kernel on the matrix cores, and its merge
+hipError_t launch_split_decode(int dtype, int block_size, int num_seqs, const AttnArgs& a,
+                               hipStream_t st, const KernelEvents& ev);
 
 hipError_t launch_multiq(int dtype, int head_dim, int block_size, int group, int num_seqs,
                          const AttnArgs& a, hipStream_t stream, const KernelEvents& ev);

@@ -1481,12 +1481,13 @@ static int mq_split_wgs_per_cu() {
   return n;
 }
 
-// The decode of an 8-bit cache at head_dim 128 through the split kernel
-// (AttnArgs without query offsets) and its merge.
-template <int B>
-static hipError_t launch_fp8_split_t(int num_seqs, const AttnArgs& a, hipStream_t st,
-                                     const KernelEvents& ev) {
-  hipError_t e = launch_main(multiq_split_kernel<PA_FP8_E4M3, B>, dim3(a.split_workgroups),
+// A decode at head_dim 128 through the split kernel (AttnArgs without query
+// offsets: one query token per sequence, pieces in (S Hk + waves) x G slots)
+// and its merge.  DT: the K/V type (the 8-bit cache runs its products in f16).
+template <int DT, int B>
+static hipError_t launch_split_decode_t(int num_seqs, const AttnArgs& a, hipStream_t st,
+                                        const KernelEvents& ev) {
+  hipError_t e = launch_main(multiq_split_kernel<DT, B>, dim3(a.split_workgroups),
                              dim3(kThreads), 0, st, ev, a);
   if (e != hipSuccess) return e;
   const int per_seq = a.num_heads * (128 / 4);
@@ -1495,13 +1496,21 @@ static hipError_t launch_fp8_split_t(int num_seqs, const AttnArgs& a, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_split_decode(int block_size, int num_seqs, const AttnArgs& a,
-                                   hipStream_t st, const KernelEvents& ev) {
+template <int DT>
+static hipError_t launch_split_decode_b(int block_size, int num_seqs, const AttnArgs& a,
+                                        hipStream_t st, const KernelEvents& ev) {
   switch (block_size) {
-    case 8: return launch_fp8_split_t<8>(num_seqs, a, st, ev);
-    case 16: return launch_fp8_split_t<16>(num_seqs, a, st, ev);
-    default: return launch_fp8_split_t<32>(num_seqs, a, st, ev);
+    case 8: return launch_split_decode_t<DT, 8>(num_seqs, a, st, ev);
+    case 16: return launch_split_decode_t<DT, 16>(num_seqs, a, st, ev);
+    default: return launch_split_decode_t<DT, 32>(num_seqs, a, st, ev);
   }
+}
+
+hipError_t launch_split_decode(int dtype, int block_size, int num_seqs, const AttnArgs& a,
+                               hipStream_t st, const KernelEvents& ev) {
+  if (dtype == PA_FP8_E4M3) return launch_split_decode_b<PA_FP8_E4M3>(block_size, num_seqs, a, st, ev);
+  if (dtype == PA_F16) return launch_split_decode_b<PA_F16>(block_size, num_seqs, a, st, ev);
+  return launch_split_decode_b<PA_BF16>(block_size, num_seqs, a, st, ev);
 }
 
 int multiq_split_workgroups_per_cu(int dtype, int block_size) {

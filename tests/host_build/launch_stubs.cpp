@@ -13,7 +13,7 @@ hipError_t launch_decode(int, int, int, int, int, const AttnArgs&, hipStream_t,
 }
 int split_workgroups_per_cu(int, int, int, int) { return 1; }
 int multiq_split_workgroups_per_cu(int, int) { return 1; }
-hipError_t launch_fp8_split_decode(int, int, const AttnArgs&, hipStream_t, const KernelEvents&) {
+hipError_t launch_split_decode(int, int, int, const AttnArgs&, hipStream_t, const KernelEvents&) {
   return hipErrorNoDevice;
 }
 hipError_t launch_multiq(int, int, int, int, int, const AttnArgs&, hipStream_t,
