@@ -103,7 +103,13 @@ size_t paged_attn_workspace_size(int num_seqs, int total_q, int max_q_len, int n
  * resident wave; pieces of one context are merged by log-sum-exp in a second
  * kernel.  partition_tokens = 0 lets the library size the pieces; a positive
  * multiple of block_size fixes each piece at that many tokens.  Batches of
- * more than 8192 sequences use fixed context partitions instead.
+ * more than 8192 sequences use fixed context partitions instead.  With
+ * partition_tokens 0 at head_dim 128 (bf16, f16, and the 8-bit cache of
+ * paged_attn_decode_fp8kv; up to 16384 (sequence, KV head) pairs) the items are
+ * 32-token tiles and the products run on the matrix cores (fp32 accumulation;
+ * P is carried to about 2^-16 in bf16 and rounded to f16 in f16); otherwise
+ * the products run on the vector ALUs in fp32.  The two agree to within that
+ * rounding, not bit for bit; a given call always takes the same one.
  */
 int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens,
