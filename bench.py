@@ -587,9 +587,9 @@ def main():
     roof["traffic"] = measured_traffic(st.name + ("_cascade" if a.cascade else "") +
                                        ("_fp8kv" if kv_fp8 else ""),
                                        res["source_hash"])
-    roof["kernel"] = ("shared-prefix cascade, whole call (prep, prefix multi-query + merge, "
-                      "tail decode + merge, combine)" if a.cascade else
-                      "multi-query main kernel" if is_multiq else "decode split kernel")
+    roof["kernel"] = ("shared-prefix decode, whole call (prefix multi-query pass, tails' decode, "
+                      "fold)" if a.cascade else
+                      "multi-query main kernel" if is_multiq else "decode main kernel (balanced split)")
     roof["algorithmic_bytes_per_launch"] = int(basis) if basis is not None else None
     if is_multiq:
         res["tflops"] = round(flops_of(st) / (call_ms * 1e-3) / 1e12, 2)
