@@ -963,14 +963,12 @@ __global__ __launch_bounds__(kThreads, 2) void multiq_mfma_rows_kernel(const Att
 }
 
 // 8-bit E4M3 K/V at head_dim 128 (the decode of an 8-bit cache through the
-// balanced split): the codes of a 32-token tile reach one of the wave's two
-// 8 KiB stages (K codes, then V codes) by direct-to-LDS loads (a wave
-// instruction moves eight 128-byte rows), and are widened to f16 on their way
-// into the operands (exact: every E4M3 value is an f16 value); the products
-// run in f16 with fp32 accumulation.  The V^T operands come straight out of
-// the code stage by 8-bit transpose reads (ds_read_b64_tr_b8: in each 16-lane
-// group, output lane j's byte r is input lane 2 r + j / 8's byte j mod 8), so
-// a stage holds only codes and two tiles are in flight per wave.
+// balanced split): the codes of a 32-token tile reach the wave's stages by
+// direct-to-LDS loads (a wave instruction moves eight 128-byte rows) and are
+// widened to f16 on their way into the operands (exact: every E4M3 value is an
+// f16 value); the products run in f16 with fp32 accumulation.  Stages: the K
+// codes (4 KiB) and the V codes (4 KiB) in one 8 KiB stage, and V widened to
+// f16 in a second 8 KiB stage with the 16-bit layout, read by transpose reads.
 template <int B>
 struct Fp8TileWalker {
   static constexpr int kRowBytes = 128;   // 128 codes
@@ -995,25 +993,17 @@ struct Fp8TileWalker {
   __device__ __forceinline__ size_t row_off(int phys, int t) const {
     return (((size_t)phys * Hk + g) * B + (t % B)) * kRowBytes;
   }
-  // 16-byte chunk positions in a stage row r: K chunk c at c ^ ((r / 2) mod 8)
-  // (the 16 rows of one lane half's K reads on distinct banks); V chunk c at
-  // c ^ vswz(r) (the eight rows of a transpose read, tokens t .. t + 3 and
-  // t + 8 .. t + 11 with t a multiple of 4, on distinct banks)
-  __device__ static __forceinline__ int vswz(int r) { return ((r >> 1) & 1) | ((r >> 2) & 2); }
   // instruction i: lane l writes stage bytes 1024 i + 16 l, i.e. row
-  // r = 8 i + l / 8 at position l % 8
-  template <bool NT>
-  __device__ __forceinline__ void load_tile(int t0, char* stage) const {
+  // r = 8 i + l / 8 at position l % 8, which holds 16-byte chunk
+  // (l % 8) ^ ((r / 2) mod 8) of K, (l % 8) ^ ((r / 2) mod 4) of V
+  template <bool NT, int MASK>
+  __device__ __forceinline__ void load_codes(const char* base, int t0, char* stage) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 8 * i + (lane >> 3);
       const int t = min(t0 + r, L - 1);   // >= t0, since t0 < L
-      const size_t ro = row_off(phys_of(t0, t), t);
-      __builtin_amdgcn_global_load_lds(kbase + ro + (((lane & 7) ^ ((r >> 1) & 7)) * 16),
-                                       (__attribute__((address_space(3))) void*)(stage + 1024 * i),
-                                       16, 0, NT ? kCpolNt : 0);
-      __builtin_amdgcn_global_load_lds(vbase + ro + (((lane & 7) ^ vswz(r)) * 16),
-                                       (__attribute__((address_space(3))) void*)(stage + 4096 + 1024 * i),
+      const char* src = base + row_off(phys_of(t0, t), t) + (((lane & 7) ^ ((r >> 1) & MASK)) * 16);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(stage + 1024 * i),
                                        16, 0, NT ? kCpolNt : 0);
     }
   }
@@ -1026,103 +1016,73 @@ struct Fp8TileWalker {
     return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
                       __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
   }
-  // This lane's LDS byte addresses in the first stage: K operand of k-step ks
-  // (lane (m, hh): codes 16 ks + 8 hh .. + 7 of row m) and the transpose read
-  // of dim block db (16-lane group q: dims 32 db + 16 (q mod 2) + 0..15,
-  // tokens 4 (q / 2) + 0..3 and 8 + 4 (q / 2) + 0..3; input lane 2 r' + b of
-  // the group addresses token r' of that list, bytes 8 b .. 8 b + 7 of the
-  // dims' chunk); the second 16-token step adds 2048.
-  __device__ __forceinline__ void lane_offsets(unsigned st, unsigned (&koff)[KS],
-                                               unsigned (&voff)[DB]) const {
+  // K operands: lane (m, hh), k-step ks: codes 16 ks + 8 hh .. + 7 of row m
+  // (chunk ks at position ks ^ ((m / 2) mod 8): the 16 rows of one lane half
+  // fall on distinct banks)
+  __device__ __forceinline__ void read_k(const char* stage, uint4 (&kr)[KS]) const {
+    typedef unsigned int u2v __attribute__((ext_vector_type(2)));
     const int m = lane & 31, hh = lane >> 5;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      koff[ks] = st + m * kRowBytes + ((ks ^ ((m >> 1) & 7)) * 16) + hh * 8;
-    const int q = lane >> 4, i = lane & 15, rr = i >> 1, b = i & 1;
-    const int tok = 4 * (q >> 1) + (rr & 3) + 8 * (rr >> 2);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int pos = ks ^ ((m >> 1) & 7);
+      const u2v x = *(__attribute__((address_space(3))) const u2v*)(
+          __attribute__((address_space(3))) const char*)(stage + m * kRowBytes + pos * 16 + hh * 8);
+      kr[ks] = widen8(x.x, x.y);
+    }
+  }
+  // V codes -> f16 rows of 256 bytes, 16-byte chunk c of row r at position
+  // c ^ 4 (r mod 4): lane l widens half l % 2 of row l / 2
+  __device__ __forceinline__ void widen_v(const char* v8, char* v16) const {
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    const int r = lane >> 1, h = lane & 1;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      voff[db] = st + 4096 + tok * kRowBytes + (((2 * db + (q & 1)) ^ vswz(tok)) * 16) + b * 8;
+    for (int j = 0; j < 4; ++j) {
+      const int c = 4 * h + j;            // codes 16 c .. 16 c + 15
+      const u4v x = *(__attribute__((address_space(3))) const u4v*)(
+          __attribute__((address_space(3))) const char*)(v8 + r * kRowBytes + ((c ^ ((r >> 1) & 3)) * 16));
+      const uint4 lo = widen8(x.x, x.y), hi = widen8(x.z, x.w);
+      *(__attribute__((address_space(3))) u4v*)(__attribute__((address_space(3))) char*)(
+          v16 + r * 256 + (((2 * c) ^ (4 * (r & 3))) * 16)) = u4v{lo.x, lo.y, lo.z, lo.w};
+      *(__attribute__((address_space(3))) u4v*)(__attribute__((address_space(3))) char*)(
+          v16 + r * 256 + (((2 * c + 1) ^ (4 * (r & 3))) * 16)) = u4v{hi.x, hi.y, hi.z, hi.w};
+    }
   }
-  // the codes of every operand of the stage at byte SO past the offsets'
-  // stage (two words per operand, widened only when used), in one asm block
-  // that ends by waiting for its own reads (the compiler would otherwise wait
-  // for every load in flight, the next tile's included, before a read it
-  // issues itself)
-  typedef unsigned int u2v __attribute__((ext_vector_type(2)));
-  template <int SO>
-  __device__ __forceinline__ void read_stage(const unsigned (&koff)[KS], const unsigned (&voff)[DB],
-                                             u2v (&k)[KS], u2v (&v)[DB][2]) const {
-    asm volatile(
-        "ds_read_b64 %0, %16 offset:%28\n\t"
-        "ds_read_b64 %1, %17 offset:%28\n\t"
-        "ds_read_b64 %2, %18 offset:%28\n\t"
-        "ds_read_b64 %3, %19 offset:%28\n\t"
-        "ds_read_b64 %4, %20 offset:%28\n\t"
-        "ds_read_b64 %5, %21 offset:%28\n\t"
-        "ds_read_b64 %6, %22 offset:%28\n\t"
-        "ds_read_b64 %7, %23 offset:%28\n\t"
-        "ds_read_b64_tr_b8 %8, %24 offset:%28\n\t"
-        "ds_read_b64_tr_b8 %9, %24 offset:%29\n\t"
-        "ds_read_b64_tr_b8 %10, %25 offset:%28\n\t"
-        "ds_read_b64_tr_b8 %11, %25 offset:%29\n\t"
-        "ds_read_b64_tr_b8 %12, %26 offset:%28\n\t"
-        "ds_read_b64_tr_b8 %13, %26 offset:%29\n\t"
-        "ds_read_b64_tr_b8 %14, %27 offset:%28\n\t"
-        "ds_read_b64_tr_b8 %15, %27 offset:%29\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=v"(k[0]), "=v"(k[1]), "=v"(k[2]), "=v"(k[3]), "=v"(k[4]), "=v"(k[5]), "=v"(k[6]),
-          "=v"(k[7]), "=v"(v[0][0]), "=v"(v[0][1]), "=v"(v[1][0]), "=v"(v[1][1]),
-          "=v"(v[2][0]), "=v"(v[2][1]), "=v"(v[3][0]), "=v"(v[3][1])
-        : "v"(koff[0]), "v"(koff[1]), "v"(koff[2]), "v"(koff[3]), "v"(koff[4]), "v"(koff[5]),
-          "v"(koff[6]), "v"(koff[7]), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
-          "i"(SO), "i"(SO + 2048)
-        : "memory");
-  }
-  // The tiles t0, t0 + 32, ... below t_end (t0 < t_end, wave-uniform) into
-  // the running (m, l, o), tile i in stage i mod 2 (the second stage
-  // kStageGap bytes past the first); the next tile's loads are in flight
-  // while one is computed.  Keys at or past lim are masked; a tile ending at
-  // or before unmask_end needs no mask.
-  static constexpr int kStageGap = 32768;
+  // The tiles t0, t0 + stride, ... below t_end, as TokenTileWalker::walk:
+  // each step reads its K operands and widens its V, then (once those LDS
+  // accesses are back) loads the next tile's codes into the same stage.
+  // kst: the K codes, then the V codes; v16: V in f16.
   template <bool NT>
-  __device__ __forceinline__ void walk(int t0, int t_end, const uint4 (&qv)[KS], float c, int lim,
-                                       int unmask_end, char* st0, f32x16_t (&o)[DB],
-                                       float& m_run, float& l_run) const {
-    char* const st1 = st0 + kStageGap;
+  __device__ __forceinline__ void walk(int t0, int t_end, int stride, const uint4 (&qv)[KS],
+                                       float c, int lim, int unmask_end, char* kst, char* v16,
+                                       f32x16_t (&o)[DB], float& m_run, float& l_run) const {
     const int hh = lane >> 5;
+    const TokenTileWalker<B> t16{nullptr, nullptr, tblc, jlast, L, Hk, g, lane};
     t_end = __builtin_amdgcn_readfirstlane(t_end);
-    unsigned koff[KS], voff[DB];
-    lane_offsets((unsigned)(size_t)(__attribute__((address_space(3))) char*)st0, koff, voff);
-    load_tile<NT>(t0, st0);
-    if (t0 + 32 < t_end) load_tile<NT>(t0 + 32, st1);
-    auto step = [&](int t, auto so) -> bool {
-      constexpr int SO = decltype(so)::value;
-      // this tile's loads: eight load instructions per later tile in flight
-      if (t + 32 < t_end) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
-      else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
-      u2v k[KS], v[DB][2];
-      read_stage<SO>(koff, voff, k, v);
+    load_codes<NT, 7>(kbase, t0, kst);
+    load_codes<NT, 3>(vbase, t0, kst + 4096);
+    for (;;) {
+      uint4 kr[KS];
+      read_k(kst, kr);
+      widen_v(kst + 4096, v16);
+      uint4 va[DB][2];
+      t16.read_vt(v16, va);
+      const bool more = t0 + stride < t_end;   // wave-uniform
       __builtin_amdgcn_sched_barrier(0);
-      if (t + 64 < t_end) load_tile<NT>(t + 64, SO ? st1 : st0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the stage is read
       __builtin_amdgcn_sched_barrier(0);
-      f32x16_t sc = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sc = Mma<PA_F16>::mma(widen8(k[ks].x, k[ks].y), qv[ks], sc);
+      if (more) {
+        load_codes<NT, 7>(kbase, t0 + stride, kst);
+        load_codes<NT, 3>(vbase, t0 + stride, kst + 4096);
+      }
+      const f32x16_t sc = tile_qk<PA_F16>(kr, qv);
       uint4 pb0, pb1, pl0, pl1;
-      tile_softmax<PA_F16>(sc, t, hh, t + 32 <= unmask_end, lim, c, m_run, l_run, o, pb0, pb1,
+      tile_softmax<PA_F16>(sc, t0, hh, t0 + 32 <= unmask_end, lim, c, m_run, l_run, o, pb0, pb1,
                            pl0, pl1);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        tile_pv<PA_F16>(o[db], widen8(v[db][0].x, v[db][0].y), widen8(v[db][1].x, v[db][1].y),
-                        pb0, pb1, pl0, pl1);
-      return t + 32 < t_end;
-    };
-    for (;;) {
-      if (!step(t0, std::integral_constant<int, 0>{})) break;
-      t0 += 32;
-      if (!step(t0, std::integral_constant<int, kStageGap>{})) break;
-      t0 += 32;
+        tile_pv<PA_F16>(o[db], va[db][0], va[db][1], pb0, pb1, pl0, pl1);
+      if (!more) break;
+      t0 += stride;
     }
   }
 };
@@ -1236,10 +1196,8 @@ __device__ __forceinline__ void mq_split_wave(const AttnArgs& a, int s, int r0, 
       const ConstI32Ptr tbl = as_const(a.block_tables + (size_t)s * a.max_blocks_per_seq);
       if constexpr (DT == PA_FP8_E4M3) {
         const Fp8TileWalker<B> w{kbase, vbase, tbl, (L - 1) / B, L, Hk, g, lane};
-        static_assert(kWaves * Wk::kStageBytes == Fp8TileWalker<B>::kStageGap,
-                      "a wave's second 8-bit stage is its V stage");
-        w.template walk<NT>(32 * j, seg_end, qv, cs, min(lrow, seg_end), min(l_tile_min, seg_end),
-                            st0, o, m_run, l_run);
+        w.template walk<NT>(32 * j, seg_end, 32, qv, cs, min(lrow, seg_end),
+                            min(l_tile_min, seg_end), st0, st1, o, m_run, l_run);
       } else {
         const Wk w{kbase, vbase, tbl, (L - 1) / B, L, Hk, g, lane};
         w.template walk<DT, NT>(32 * j, seg_end, 32, qv, cs, min(lrow, seg_end),
