@@ -52,6 +52,28 @@ def test_append_is_bit_exact(dtype, D, B):
     assert np.array_equal(_bits(W.torch_to_host(t["v_cache"], dtype)), _bits(wv))
 
 
+@pytest.mark.parametrize("Hk,D,dtype", [(3, 128, "f32"), (8, 128, "f32"), (16, 128, "f32"),
+                                        (12, 128, "bf16"), (5, 64, "bf16")])
+def test_append_wide_rows(Hk, D, dtype):
+    """Tokens of 96, 256, 512, 192 and 40 16-byte chunks: a wave's full passes over a
+    token's rows (loaded before the lookup) and the chunks past them."""
+    B = 16
+    st = W.random_small(900 + Hk, num_seqs=5, num_heads=Hk, num_kv_heads=Hk, head_dim=D,
+                        block_size=B, ctx_lo=1, ctx_hi=200, q_len_max=9, dtype=dtype)
+    U.say(f"append wide {dtype} Hk={Hk} D={D} ctx={list(st.context_lens)} n={list(st.q_lens)}")
+    vals = W.host_values(st)
+    rng = np.random.default_rng(Hk * D)
+    kn, vn = (_new_rows(rng, st.total_q, Hk, D, dtype) for _ in range(2))
+    t = U.upload(st, {**vals, "k_new": kn, "v_new": vn})
+    U.ops().append(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["block_tables"],
+                   t["context_lens"], t["q_offsets"], st.max_context_len)
+    torch.cuda.synchronize()
+    wk, wv = OK.append_kv(vals["k_cache"], vals["v_cache"], kn, vn, st.block_tables,
+                          st.context_lens, st.q_offsets, B)
+    assert np.array_equal(_bits(W.torch_to_host(t["k_cache"], dtype)), _bits(wk))
+    assert np.array_equal(_bits(W.torch_to_host(t["v_cache"], dtype)), _bits(wv))
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_copy_blocks_is_bit_exact(dtype):
     st = W.random_small(77, num_seqs=4, num_heads=8, num_kv_heads=4, head_dim=128,
