@@ -18,6 +18,12 @@
  *  - All array pointers are DEVICE pointers owned by the caller.  The library
  *    allocates nothing, keeps no pointer after return, and never synchronizes:
  *    work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *    The device work of a call is kernel launches only (no memory sets or
+ *    copies; any plan is computed on the device), so a call may be captured
+ *    into a HIP graph, its output and workspace given, and replayed: every
+ *    replay gives the same bytes as the call made directly.  The first call
+ *    on a device (made outside a capture) fills the library's per-device
+ *    caches (compute units, occupancies, the allocation-free scratch address).
  *  - Element counts are in elements, byte counts in bytes.
  *  - Pool layout: k_cache and v_cache are separate, contiguous
  *        [num_blocks][num_kv_heads][block_size][head_dim]
