@@ -295,6 +295,26 @@ def _sample(st, k, seed):
     return sorted(pick)
 
 
+@pytest.mark.parametrize("S,H,Hk", [(8200, 8, 2), (2100, 32, 8)])
+def test_decode_past_split_limits(S, H, Hk):
+    """Past the balanced split's limits: more than 8192 sequences (partitions and
+    their merge instead), and more than 16,384 (sequence, KV head) units at head_dim
+    128 (the vector-ALU split instead of the matrix-core one).  Sampled sequences,
+    the first and last among them, against the oracle; the bf16 output is the
+    rounded fp32 one."""
+    st = W.random_small(40 + S, num_seqs=S, num_heads=H, num_kv_heads=Hk, head_dim=128,
+                        block_size=16, ctx_lo=1, ctx_hi=40, dtype="bf16")
+    U.say(f"decode past split limits S={S} H={H} Hk={Hk} ctx<={st.max_context_len}")
+    vals = W.host_values(st)
+    t = U.upload(st, vals)
+    out32 = U.run_decode(st, t, out_dtype=torch.float32)
+    U.assert_rounds(U.run_decode(st, t), out32, f"S={S}")
+    rng = np.random.default_rng(S)
+    sample = sorted({0, S - 1, *rng.choice(S, 150, replace=False).tolist()})
+    want = U.oracle_decode(st, vals, seqs=sample)
+    U.assert_close(out32, want, "bf16", f"S={S} sampled", rows=sample)
+
+
 def _full_size(st, layers=(0,)):
     """The benchmark's inputs (device-generated; for a multi-layer pool the queries of
     layer 0 and the K/V pool of each listed layer, as the benchmark pairs them), its
