@@ -56,6 +56,25 @@ def test_fp8kv_decode(D, B, G):
         U.assert_rounds(_run(st, t, ks, vs), out32, f"scales {ks},{vs} bf16 out")
 
 
+def test_fp8kv_past_matrix_core_split_limit():
+    """More (sequence, KV head) units than the matrix-core split takes (16,384): the
+    vector-ALU 8-bit decode instead.  Sampled sequences against the oracle."""
+    S = 2100
+    st = W.random_small(70, num_seqs=S, num_heads=32, num_kv_heads=8, head_dim=128,
+                        block_size=16, ctx_lo=1, ctx_hi=40, dtype="bf16")
+    vals = W.host_values(st)
+    k8, v8 = _to_codes(vals["k_cache"]), _to_codes(vals["v_cache"])
+    t = U.upload(st, {"q": vals["q"]})
+    t["k8"], t["v8"] = torch.from_numpy(k8).to(U.DEV), torch.from_numpy(v8).to(U.DEV)
+    U.say(f"fp8 kv past split limit S={S}")
+    rng = np.random.default_rng(S)
+    sample = sorted({0, S - 1, *rng.choice(S, 150, replace=False).tolist()})
+    want = OP.paged_decode_quant_kv(vals["q"], "bf16", k8, v8, "fp8e4m3", 0.37, 2.5,
+                                    st.block_tables, st.context_lens, 16, st.scale, seqs=sample)
+    out = _run(st, t, 0.37, 2.5, torch.float32)
+    U.assert_close(out, want, "bf16", "fp8 past split limit", rows=sample)
+
+
 def test_fp8kv_forced_pieces_and_edges():
     """Small forced chunks (pieces and merges) and edge context lengths."""
     B = 16

@@ -212,6 +212,25 @@ def test_multiq_split_ragged_rows_and_empty_sequences(dtype, B):
     assert np.max(np.abs(out[rows] - want[rows])) <= U.TOL[dtype]
 
 
+@pytest.mark.parametrize("S,H,Hk", [(8200, 8, 2), (3000, 32, 8)])
+def test_multiq_past_split_limits(S, H, Hk):
+    """Past the multi-query split's limits (more than 8192 sequences; more than
+    16,384 (sequence, KV head, row tile) units): the partitioned kernels instead.
+    Sampled sequences, the first and last among them, against the oracle."""
+    st = W.random_small(60 + S, num_seqs=S, num_heads=H, num_kv_heads=Hk, head_dim=128,
+                        block_size=16, ctx_lo=3, ctx_hi=40, q_len_max=3, dtype="bf16")
+    assert not _ops().multiq_uses_split(S, st.max_q_len, H, Hk, 128, torch.bfloat16)
+    U.say(f"multiq past split limits S={S} H={H} Hk={Hk}")
+    vals = W.host_values(st)
+    t = U.upload(st, vals)
+    out = U.run_multiq(st, t, out_dtype=torch.float32)
+    rng = np.random.default_rng(S)
+    sample = sorted({0, S - 1, *rng.choice(S, 150, replace=False).tolist()})
+    want = U.oracle_multiq(st, vals, seqs=sample)
+    rows = np.concatenate([np.arange(st.q_offsets[s], st.q_offsets[s + 1]) for s in sample])
+    U.assert_close(out, want, "bf16", f"S={S} sampled", rows=rows)
+
+
 def test_multiq_split_shared_blocks_and_negative_scale():
     """Sequences sharing a prefix of blocks (more table entries than pool blocks: the
     loads keep their cache lines) and a negative softmax scale."""
