@@ -10,9 +10,11 @@ it put the K-operand reads ahead of its own wait and the outputs were wrong.
 This test compiles the source that uses such loads to gfx950 assembly with the
 library's own flags and checks, in each kernel's instruction order, that no
 ds_read comes after a global_load_lds without an s_waitcnt on vmcnt in
-between.  It is a coarse check (it follows the text, not the control flow, and
-takes any vmcnt wait as sufficient), meant to catch that class of mistake on the
-CPU before a run on the device."""
+between, and that around every loop the reads at its head wait when loads are
+still in flight on its back edge.  It is a coarse check (it follows the text and
+the loops' back edges, not every branch, and takes any vmcnt wait as
+sufficient), meant to catch that class of mistake on the CPU before a run on the
+device."""
 import os
 import re
 import shutil
@@ -25,23 +27,53 @@ from paged_kv_cache_289_amd import build as B
 SRC = os.path.join(B.CSRC, "pa_multiq.hip")
 
 
-def unwaited_lds_reads(asm: str):
-    """(kernel, line) of each LDS read reached, in text order within its kernel,
-    after a direct-to-LDS load with no vmcnt wait since."""
-    out, name, pending = [], None, False
-    for n, line in enumerate(asm.splitlines()):
-        m = re.match(r"^(_Z\w+):", line)
-        if m:
-            name, pending = m.group(1), False
-            continue
-        t = line.strip()
+def _functions(lines):
+    """(name, first line, end line) of each kernel in the assembly."""
+    starts = [(i, m.group(1)) for i, l in enumerate(lines) for m in [re.match(r"^(_Z\w+):", l)]
+              if m]
+    ends = [i for i, l in enumerate(lines) if l.startswith(".Lfunc_end")]
+    for k, (i, name) in enumerate(starts):
+        nxt = starts[k + 1][0] if k + 1 < len(starts) else len(lines)
+        end = min(next((e for e in ends if e > i), len(lines)), nxt)
+        yield name, i, end
+
+
+def _scan(body, pending):
+    """Walk instructions in order from a pending state; returns (reads hit while
+    pending, pending at the end)."""
+    hits = []
+    for n, t in body:
         if t.startswith("global_load_lds"):
             pending = True
         elif t.startswith("s_waitcnt") and "vmcnt" in t:
             pending = False
         elif t.startswith("ds_read") and pending:
-            out.append((name, n))
-    return out
+            hits.append(n)
+    return hits, pending
+
+
+def unwaited_lds_reads(asm: str):
+    """(kernel, line) of each LDS read reached after a direct-to-LDS load with no
+    vmcnt wait since: in text order within each kernel, and around each loop,
+    from its back edge (a branch to an earlier label) to the reads at its head."""
+    lines = asm.splitlines()
+    out = set()
+    for name, i0, i1 in _functions(lines):
+        body = [(n, lines[n].strip()) for n in range(i0 + 1, i1)]
+        hits, _ = _scan(body, False)
+        out.update((name, n) for n in hits)
+        label_at = {t.split(":")[0]: k for k, (n, t) in enumerate(body)
+                    if re.match(r"^\.LBB\w+:", t)}
+        for k, (n, t) in enumerate(body):
+            m = re.match(r"^s_(?:c)?branch\w*\s+(\.LBB\w+)$", t)
+            if not m or m.group(1) not in label_at or label_at[m.group(1)] >= k:
+                continue
+            h = label_at[m.group(1)]
+            _, pending = _scan(body[h:k + 1], False)
+            if pending:   # loads in flight on the back edge: the head's reads must wait
+                hits, _ = _scan(body[h:k + 1], True)
+                out.update((name, x) for x in hits)
+    return sorted(out)
 
 
 def test_scan_flags_a_read_before_the_wait():
@@ -57,6 +89,30 @@ def test_scan_flags_a_read_before_the_wait():
         "\tds_read_b64_tr_b16 v[2:3], v6",
     ])
     assert unwaited_lds_reads(asm) == [("_Zk", 2)]
+
+
+def test_scan_follows_a_loop_back_edge():
+    """A loop whose head reads before its wait, with the next tile's loads issued
+    at its tail: the reads are reached unwaited through the back edge."""
+    asm = "\n".join([
+        "_Zloop:",
+        "\tglobal_load_lds_dwordx4 v[0:1], off",
+        "\ts_waitcnt vmcnt(0)",
+        ".LBB0_1:",
+        "\tds_read_b128 v[2:5], v6",
+        "\ts_waitcnt vmcnt(0)",
+        "\tds_read_b64_tr_b16 v[8:9], v6",
+        "\tglobal_load_lds_dwordx4 v[0:1], off",
+        "\ts_cbranch_scc1 .LBB0_1",
+        "_Zok:",
+        "\tglobal_load_lds_dwordx4 v[0:1], off",
+        ".LBB1_1:",
+        "\ts_waitcnt vmcnt(0)",
+        "\tds_read_b128 v[2:5], v6",
+        "\tglobal_load_lds_dwordx4 v[0:1], off",
+        "\ts_cbranch_scc1 .LBB1_1",
+    ])
+    assert unwaited_lds_reads(asm) == [("_Zloop", 4)]
 
 
 @pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None,
