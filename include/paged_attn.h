@@ -418,13 +418,17 @@ int paged_seq_match_prefix(paged_block_pool* pool, int seq, const int32_t* token
 
 /*
  * Measurement aid, not part of the attention path: one plain streaming read of
- * `bytes` bytes (a multiple of 16) at `buf` (16-byte aligned), 16-byte vectors
- * in a grid-stride loop over `workgroups` workgroups of 256 threads (0 = eight
- * per compute unit), with the non-temporal hint when `nontemporal` is nonzero.
- * It gives the HBM read rate this device sustains, the practical ceiling to set
- * the paged kernels' bandwidth figures against.  `sink` (one uint32, device) is
- * written only by a data-dependent branch that keeps the loads live; its value
- * means nothing.  Errors as for the other entry points.
+ * `bytes` bytes (a multiple of 16) at `buf` (16-byte aligned) by `workgroups`
+ * workgroups of 256 threads.  `nontemporal` selects the pattern: 0, 16-byte
+ * vectors in a grid-stride loop (0 workgroups = eight per compute unit); 1, the
+ * same with the non-temporal hint; 2, each wave its own contiguous share in
+ * 8 KiB steps by direct-to-LDS loads with the non-temporal hint, two stages per
+ * wave (0 workgroups = two per compute unit; the bytes past the waves' shares in
+ * a grid-stride loop).  Other values give PA_ERR_SHAPE.  It gives the HBM read
+ * rate this device sustains, the practical ceiling to set the paged kernels'
+ * bandwidth figures against.  `sink` (one uint32, device) is written only by a
+ * data-dependent branch that keeps the loads live; its value means nothing.
+ * Errors as for the other entry points.
  */
 int paged_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups,
                    int nontemporal, pa_stream_t stream);

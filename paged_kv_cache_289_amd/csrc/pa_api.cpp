@@ -834,8 +834,9 @@ int paged_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups
   if (bytes == 0) return PA_OK;
   if (!buf || !sink) return PA_ERR_NULL;
   if (bytes % 16 != 0 || !aligned16(buf)) return PA_ERR_UNSUPPORTED;
-  if (workgroups < 0) return PA_ERR_SHAPE;
-  if (workgroups == 0) workgroups = device_cus() * 8;
+  if (workgroups < 0 || nontemporal < 0 || nontemporal > 2) return PA_ERR_SHAPE;
+  // (the direct-to-LDS mode holds 64 KiB of LDS per workgroup: two per CU)
+  if (workgroups == 0) workgroups = device_cus() * (nontemporal == 2 ? 2 : 8);
   hipError_t e = pa::launch_stream_read(buf, bytes, sink, workgroups, nontemporal,
                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;

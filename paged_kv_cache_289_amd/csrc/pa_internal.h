@@ -147,8 +147,10 @@ struct CascadeFold {
 };
 hipError_t launch_cascade_fold(const CascadeFold& f, int head_dim, hipStream_t stream);
 
+// mode 0: grid-stride, cached loads; 1: grid-stride, non-temporal; 2: each
+// wave its own contiguous share through direct-to-LDS loads (non-temporal)
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int workgroups,
-                              int nontemporal, hipStream_t stream);
+                              int mode, hipStream_t stream);
 
 // Device scratch of the allocation-free decode entry point: kScratchBytes in
 // a file-scope device array, one copy per GPU (pa_noalloc.hip).  Returns the

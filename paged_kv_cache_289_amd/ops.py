@@ -562,11 +562,12 @@ class BlockPool:
                         LIB.paged_seq_match_prefix(self._h, int(seq), buf, len(tokens)))
 
 
-def hbm_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, nontemporal: bool = False,
+def hbm_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, mode: int = 0,
              stream=None):
-    """One streaming read of all of ``buf`` (a measurement aid: the device's HBM read rate)."""
+    """One streaming read of all of ``buf`` (a measurement aid: the device's HBM read rate).
+    ``mode``: 0 grid-stride, 1 grid-stride non-temporal, 2 per-wave runs through LDS."""
     _need_contig(buf=buf)
     rc = LIB.paged_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
-                            int(workgroups), 1 if nontemporal else 0, _stream(stream))
+                            int(workgroups), int(mode), _stream(stream))
     _check("paged_hbm_read", rc)
 

@@ -152,6 +152,15 @@ def test_gather_and_check_reject_bad_arguments_on_host():
         ops.PA_ERR_SHAPE
 
 
+def test_hbm_read_rejects_unknown_patterns_on_host():
+    L = ops.LIB
+    assert L.paged_hbm_read(FAKE, 4096, FAKE, 0, 3, None) == ops.PA_ERR_SHAPE
+    assert L.paged_hbm_read(FAKE, 4096, FAKE, 0, -1, None) == ops.PA_ERR_SHAPE
+    assert L.paged_hbm_read(FAKE, 4096, FAKE, -1, 0, None) == ops.PA_ERR_SHAPE
+    assert L.paged_hbm_read(FAKE, 4095, FAKE, 0, 2, None) == ops.PA_ERR_UNSUPPORTED
+    assert L.paged_hbm_read(None, 4096, FAKE, 0, 2, None) == ops.PA_ERR_NULL
+
+
 def test_workspace_size_formula():
     # Decode, 64 sequences x 8 KV heads (G = 4), head_dim 128, contexts up to 4096 in
     # 16-token blocks, 256-token pieces: each (sequence, KV head) is at most 256 block
