@@ -162,7 +162,7 @@ bool mq_split_shape(int num_seqs, int max_q_len, int num_heads, int num_kv_heads
 // (fewer where fewer are resident), in whole workgroups.  The workspace is
 // sized for the device-independent bound.
 int mq_split_waves(int64_t units, int max_context_len, int resident) {
-  const int64_t items = units * (ceil_div(max_context_len, 32) + pa::kMqSegItems);
+  const int64_t items = units * (ceil_div(max_context_len, 32) + pa::kMqSegItemsMax);
   const int64_t w =
       std::max<int64_t>(1, std::min<int64_t>(items, std::min(resident, pa::kMqMaxSplitWaves)));
   return (int)((w + pa::kWaves - 1) / pa::kWaves * pa::kWaves);

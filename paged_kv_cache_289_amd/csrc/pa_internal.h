@@ -40,10 +40,11 @@ constexpr int kSegItems = PA_SEG_ITEMS;
 // 128): the fixed cost per (sequence, KV head, row tile) in 32-token tiles, the
 // most waves launched and the most units (sequence x KV head x row tile) they
 // take (the workspace holds a 32-row piece per unit and per wave).
-#ifndef PA_MQ_SEG_ITEMS
-#define PA_MQ_SEG_ITEMS 2
-#endif
-constexpr int kMqSegItems = PA_MQ_SEG_ITEMS;
+// It is larger for an 8-bit cache, whose key tiles take half the bytes (and so
+// less time) of a 16-bit one against the same fixed cost; kMqSegItemsMax bounds
+// it for the host's sizing.
+constexpr int mq_seg_items(int kv_dtype) { return kv_dtype == PA_FP8_E4M3 ? 4 : 2; }
+constexpr int kMqSegItemsMax = 4;
 constexpr int kMqMaxSplitWaves = 4096;
 constexpr int kMqMaxSplitUnits = 16384;
 

@@ -1114,11 +1114,11 @@ __device__ __forceinline__ void load_q_operand_f16(const void* q, size_t out_row
 // ---------------------------------------------------------------------------
 // Units are (sequence s, KV head g, row tile rt): R_s = ceil(n_s G / 32) row
 // tiles per KV head.  Each unit of a sequence with n_s > 0 rows and L_s > 0
-// keys costs c_s = nt_s + kMqSegItems items: its nt_s = ceil(L_s / 32) key
+// keys costs c_s = nt_s + X items: its nt_s = ceil(L_s / 32) key
 // tiles plus a fixed cost (the query load, the first tile's latency, the
 // stores).  Items are numbered f = pre[s] + (g R_s + rt) c_s + k (pre:
 // exclusive prefix sums of Hk R_s c_s); wave w takes f in [w chunk,
-// (w + 1) chunk), item k >= kMqSegItems being key tile k - kMqSegItems.  So
+// (w + 1) chunk), item k >= X being key tile k - X (X = mq_seg_items(DT)).  So
 // every wave does the same work whatever the mix of context lengths, with no
 // partition size to choose.  A wave that covers all of a unit's tiles writes
 // its rows' outputs; otherwise it leaves its piece (max, sum, unnormalised O
@@ -1147,7 +1147,7 @@ template <int DT, int B, bool NT>
 __device__ __forceinline__ void mq_split_wave(const AttnArgs& a, int s, int r0, int f, int f_end,
                                               int wid, char* st0, char* st1) {
   using Wk = TokenTileWalker<B>;
-  constexpr int D = 128, KS = Wk::KS, DB = Wk::DB, X = kMqSegItems;
+  constexpr int D = 128, KS = Wk::KS, DB = Wk::DB, X = mq_seg_items(DT);
   const int H = a.num_heads, Hk = a.num_kv_heads, G = a.group;
   const int Rmax = (a.max_q_len * G + 31) / 32;
   // rows per piece slot: a row tile, or for a decode the group's G rows
@@ -1251,7 +1251,7 @@ __device__ __forceinline__ void mq_split_wave(const AttnArgs& a, int s, int r0, 
 template <int DT, int B>
 __global__ __launch_bounds__(kThreads, 2) void multiq_split_kernel(const AttnArgs a) {
   using Wk = TokenTileWalker<B>;
-  constexpr int X = kMqSegItems;
+  constexpr int X = mq_seg_items(DT);
   // the waves' K stages, then their V stages; before the walk the same LDS
   // holds the prefix sums (kMaxSplitSeqs + 1 ints fit)
   __shared__ __attribute__((aligned(16))) char sm_stage[2 * kWaves * Wk::kStageBytes];
@@ -1348,10 +1348,11 @@ __global__ __launch_bounds__(kThreads, 2) void multiq_split_kernel(const AttnArg
 // (query token, head) of sequence blockIdx.y.  Its row r = i G + h of KV head
 // g is row r % 32 of row tile rt = r / 32; that unit's items are
 // [a0, a0 + c) with a0 = pre[s] + (g R + rt) c, its tiles the last
-// c - kMqSegItems, so the waves (a0 + kMqSegItems) / chunk ..
+// c - X (X: the fixed cost of the split kernel's K/V type), so the waves
+// (a0 + X) / chunk ..
 // (a0 + c - 1) / chunk covered it, wave w leaving its piece in slot
 // (s Hk + g) Rmax + rt + w.  Sequences without keys get zero rows.
-template <int D>
+template <int D, int X>
 __global__ __launch_bounds__(256) void mq_split_merge_kernel(const AttnArgs a) {
   constexpr int kChunks = D / 4;
   const int H = a.num_heads, Hk = a.num_kv_heads, G = a.group;
@@ -1376,9 +1377,9 @@ __global__ __launch_bounds__(256) void mq_split_merge_kernel(const AttnArgs a) {
   const int r = qi * G + h, rt = r / 32, row = r % 32;
   const ConstI32Ptr plan = as_const(a.plan);
   const int chunk = plan[0];
-  const int c = sh.nt + kMqSegItems;
+  const int c = sh.nt + X;
   const int a0 = plan[2 + s] + (g * sh.R + rt) * c;
-  const int w0 = (a0 + kMqSegItems) / chunk, w1 = (a0 + c - 1) / chunk;
+  const int w0 = (a0 + X) / chunk, w1 = (a0 + c - 1) / chunk;
   if (w0 == w1) return;                // written by its one wave
   const size_t base = (size_t)(s * Hk + g) * Rmax + rt;
   constexpr int kBatch = 8;
@@ -1431,8 +1432,8 @@ static hipError_t launch_mfma_t(int num_seqs, const AttnArgs& a, hipStream_t st,
                                  dim3(kThreads), 0, st, ev, a);
       if (e != hipSuccess) return e;
       const int per_seq = a.max_q_len * a.num_heads * (D / 4);
-      hipLaunchKernelGGL((mq_split_merge_kernel<D>), dim3((per_seq + 255) / 256, num_seqs),
-                         dim3(256), 0, st, a);
+      hipLaunchKernelGGL((mq_split_merge_kernel<D, mq_seg_items(DT)>),
+                         dim3((per_seq + 255) / 256, num_seqs), dim3(256), 0, st, a);
       return hipGetLastError();
     }
   }
@@ -1491,8 +1492,8 @@ static hipError_t launch_split_decode_t(int num_seqs, const AttnArgs& a, hipStre
                              dim3(kThreads), 0, st, ev, a);
   if (e != hipSuccess) return e;
   const int per_seq = a.num_heads * (128 / 4);
-  hipLaunchKernelGGL((mq_split_merge_kernel<128>), dim3((per_seq + 255) / 256, num_seqs),
-                     dim3(256), 0, st, a);
+  hipLaunchKernelGGL((mq_split_merge_kernel<128, mq_seg_items(DT)>),
+                     dim3((per_seq + 255) / 256, num_seqs), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

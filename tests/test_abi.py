@@ -181,9 +181,10 @@ def test_workspace_size_formula():
     assert ops.workspace_size(2, 10, 5, 32, 8, 128, 16, 256, 256) == 0
     # ... while the library's own split (5 tokens x G 4 = 20 rows: one row tile per
     # KV head) holds a 32-row piece per (sequence, KV head, row tile) unit and per
-    # wave: 2*8 = 16 units of 256/32 + 2 items each = 160 waves at most; the plan
-    # (2 + 3 int32, on 256 bytes), then fp32 (max, sum) and 128 outputs per row
-    rows = (16 + 160) * 32
+    # wave: 2*8 = 16 units of 256/32 + 4 items each (the sizing takes the larger
+    # fixed cost, an 8-bit cache's) = 192 waves at most; the plan (2 + 3 int32, on
+    # 256 bytes), then fp32 (max, sum) and 128 outputs per row
+    rows = (16 + 192) * 32
     assert ops.workspace_size(2, 10, 5, 32, 8, 128, 16, 256, 0) == \
         256 + rows * 2 * 4 + rows * 128 * 4
     # the waves stop at 4096 (64 sequences of up to 8192 keys)
